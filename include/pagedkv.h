@@ -1,0 +1,185 @@
+/*
+ * pagedkv.h — C ABI of libpagedkv.so: attention over a paged KV cache on AMD MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [vLLM-internals]  "Phase 17 · 04 — vLLM serving internals" (aiengineeringfromscratch.com),
+ *                     PagedAttention section: fixed 16-token KV blocks, one block table per
+ *                     sequence mapping logical token positions to physical block ids.
+ *   [C13-L2]          "C13 推理 · 第2课 服务端:连续批处理与 PagedAttention" (geekvape-learning),
+ *                     section 改进二:PagedAttention, figure 按块表取 K and its dimension table:
+ *                     one pool per layer of blocks x block size x (KV heads x head dim); a
+ *                     request's keys (and values) are the pool rows gathered through its table.
+ *   [Chunked-Prefill] "Chunked Prefill" (Ultralytics glossary): prefill stores the prompt's K/V in
+ *                     the cache and decode reads the whole cache each step (section on prefill and
+ *                     decode); each chunk attends under a causal mask over absolute positions to the
+ *                     cached K/V of all earlier chunks plus its own tokens (section on how chunked
+ *                     prefill works, with its PyTorch example).
+ *   [Engine-core]     "第2章:推理引擎核心技术" (aiinfra.vidrealm.tech), §1.2 (block-table example:
+ *                     logical block j holds tokens 16j..16j+15) and §1.4 (the paged kernel walks a
+ *                     request's pages through the table and accumulates with an online softmax).
+ *
+ * Data layout shared by every call (all device memory, caller-owned):
+ *   key_pool, value_pool  [num_blocks, 16, num_kv_heads, head_dim], row-major, same dtype.  A
+ *                         "slot" is one token row of num_kv_heads*head_dim elements at flat row
+ *                         index block*16 + offset.
+ *   block_tables          int32 [num_seqs, max_blocks_per_seq], row-major.  Entry [s][j] is the
+ *                         physical block of sequence s's tokens 16j..16j+15.  Entries past the
+ *                         sequence's last live block are never read and may hold anything.
+ *   query / out           [rows, num_q_heads, head_dim], contiguous.
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions:
+ *   - Device pointers are device memory; int arguments are host values.  `stream` is a
+ *     hipStream_t (NULL = the null stream).  Every call only enqueues work on `stream` and returns;
+ *     buffers must stay alive until the stream reaches the call.  No call synchronises, allocates
+ *     or keeps state between calls (the only cached state is each device's compute-unit count).
+ *   - Calls return a pkv_status.  Argument errors are found on the host before any HIP call.
+ *     PKV_ERR_HIP reports a failed launch (hipGetLastError).  No C++ exception crosses the ABI.
+ *   - err_flag: if non-NULL (a device int32, zeroed by the caller), kernels check every block id
+ *     and slot they read against the pool and OR a PKV_FLAG_* bit into *err_flag instead of
+ *     touching memory out of range; the affected output is then unspecified.  With err_flag ==
+ *     NULL the checks are skipped and out-of-range ids are undefined behaviour.
+ *   - Empty work (num_tokens == 0, num_seqs == 0) is a successful no-op.
+ *   - Supported: head_dim in {64, 128, 256}; num_q_heads % num_kv_heads == 0 and
+ *     num_q_heads / num_kv_heads <= 16; block_size == 16.  Cache write and decode take fp32 or
+ *     bf16; the prefill chunk takes bf16 (bf16 MFMA with fp32 accumulation).  Outputs may be
+ *     fp32 or bf16 (round to nearest even); accumulation is always fp32.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,         /* null pointer, negative size, inconsistent shapes */
+  PKV_ERR_UNSUPPORTED = 2,         /* dtype, head_dim, head ratio or block size outside the list above */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below pkv_decode_workspace_bytes() */
+  PKV_ERR_HIP = 4                  /* a kernel launch failed */
+} pkv_status;
+
+typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1 } pkv_dtype;
+
+/* Bits OR-ed into *err_flag by checked kernels. */
+#define PKV_FLAG_BAD_BLOCK 1   /* a block-table entry the call had to read is outside [0, num_blocks) */
+#define PKV_FLAG_BAD_SLOT 2    /* a slot is >= num_blocks * 16 */
+#define PKV_FLAG_BAD_LENGTH 4  /* a context / chunk end exceeds max_blocks_per_seq * 16, or is negative */
+
+/* Static description of a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/*
+ * Slot mapping ([Engine-core] §1.2; [vLLM-internals] PagedAttention section).
+ * For every sequence s and i < cu_new_lens[s+1] - cu_new_lens[s], with absolute position
+ * p = start_pos[s] + i:
+ *     slot_mapping[cu_new_lens[s] + i] = block_tables[s][p / 16] * 16 + p % 16.
+ *   slot_mapping  out, int32 [cu_new_lens[num_seqs]]
+ *   cu_new_lens   int32 [num_seqs + 1], non-decreasing, cu_new_lens[0] == 0 (device)
+ *   start_pos     int32 [num_seqs] (device)
+ *   max_new_len   host upper bound of cu_new_lens[s+1] - cu_new_lens[s] (sizes the grid; tokens
+ *                 beyond it are not mapped)
+ * A position past the table (p / 16 >= max_blocks_per_seq) or a bad block id yields slot -1
+ * and, with err_flag, PKV_FLAG_BAD_LENGTH / PKV_FLAG_BAD_BLOCK.
+ */
+pkv_status pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* cu_new_lens, const int32_t* start_pos, int32_t num_seqs,
+                            int32_t max_new_len, int32_t num_blocks, int32_t block_size, int32_t* err_flag,
+                            void* stream);
+
+/*
+ * Cache write ([Chunked-Prefill], section on prefill and decode: the new tokens' K/V are stored in
+ * the cache; [C13-L2]: each generated token fills one slot).
+ * For t < num_tokens with slot = slot_mapping[t] >= 0: the key row key[t] (num_kv_heads*head_dim
+ * elements, contiguous, token stride key_tok_stride elements) is copied bit for bit into
+ * key_pool slot `slot`, and likewise value[t] into value_pool.  Negative slots are skipped.
+ * Duplicate slots within one call are a caller error (which copy wins is unspecified).
+ *   key, value        [num_tokens, num_kv_heads, head_dim] with the given token strides (in
+ *                     elements, >= num_kv_heads*head_dim); same dtype as the pools; no conversion.
+ *   num_blocks        pool size in blocks (used by the err_flag check).
+ */
+pkv_status pkv_cache_write(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                           void* key_pool, void* value_pool, const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           pkv_dtype dtype, int32_t* err_flag, void* stream);
+
+/*
+ * Paged gather ([C13-L2] figure 按块表取 K: K_r = gather(K_pool, table_r), values alike).
+ * Copies sequence s's first lengths[s] token rows of both pools, in logical order, into
+ * key_out / value_out rows cu_out[s] .. cu_out[s] + lengths[s] - 1, bit for bit, using the same
+ * address arithmetic as the attention kernels.  A diagnostic used to test block indexing.
+ *   key_out, value_out  [cu_out[num_seqs], num_kv_heads, head_dim], pool dtype
+ *   lengths, cu_out     int32 [num_seqs] and [num_seqs + 1] (device)
+ *   max_len             host upper bound of lengths[s] (sizes the grid)
+ */
+pkv_status pkv_paged_gather(void* key_out, void* value_out, const void* key_pool, const void* value_pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* lengths,
+                            const int32_t* cu_out, int32_t num_seqs, int32_t max_len, int32_t num_blocks,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                            int32_t* err_flag, void* stream);
+
+/*
+ * Decode split size, in tokens, that pkv_paged_attn_decode uses for these shapes when called with
+ * split_tokens == 0 (a multiple of 128).  Depends on the arguments only.
+ */
+int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq);
+
+/*
+ * Workspace bytes pkv_paged_attn_decode needs for these shapes and split size (0 = the default
+ * above): per (sequence, query head, split) an fp32 partial output row plus its running max and
+ * normaliser.  Returns 0 for invalid shapes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t split_tokens);
+
+/*
+ * One-token paged decode ([Chunked-Prefill] section on prefill and decode: decode reads the whole
+ * cache; [Engine-core] §1.4: walk the request's pages through the table, online softmax).
+ * out[s][h] = sum_j softmax_j(scale * q[s][h] . K_s[j]) V_s[j] over positions j < context_lens[s]
+ * of sequence s's cache, KV head h / (num_q_heads / num_kv_heads).  context_lens[s] counts the
+ * current token, which must already be in the cache.  context_lens[s] == 0 gives a zero row.
+ * Long contexts are cut into splits of split_tokens positions whose partial results are merged
+ * with a log-sum-exp combine; results do not depend on the split size beyond fp32 rounding.
+ *   out                 [num_seqs, num_q_heads, head_dim], dtype out_dtype
+ *   query               [num_seqs, num_q_heads, head_dim], dtype `dtype` (the pool dtype)
+ *   context_lens        int32 [num_seqs] (device), each <= max_blocks_per_seq * 16
+ *   split_tokens        0 for the default, else a positive multiple of 128
+ *   workspace           device scratch of >= pkv_decode_workspace_bytes(...) bytes; contents on
+ *                       entry are ignored; must not be shared by calls running concurrently.
+ */
+pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                 const void* value_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, float scale,
+                                 pkv_dtype dtype, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                 int32_t* err_flag, void* stream);
+
+/*
+ * Chunked-prefill attention ([Chunked-Prefill], section on how chunked prefill works and its
+ * PyTorch example).  Sequence s owns query rows cu_q_lens[s] .. cu_q_lens[s+1]-1; row i of it sits
+ * at absolute position chunk_offsets[s] + i, and the cache must already hold positions
+ * 0 .. chunk_offsets[s] + L_s - 1 (earlier chunks plus this chunk, written by pkv_cache_write).
+ * Causal: row i attends to positions 0 .. chunk_offsets[s] + i.  Non-causal: to all positions
+ * 0 .. chunk_offsets[s] + L_s - 1.
+ *   out, query          [cu_q_lens[num_seqs], num_q_heads, head_dim]; query bf16, out out_dtype
+ *   cu_q_lens           int32 [num_seqs + 1] (device), non-decreasing from 0
+ *   chunk_offsets       int32 [num_seqs] (device), >= 0
+ *   max_q_len           host upper bound of L_s (sizes the grid; rows beyond it are not computed)
+ */
+pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* query, const int32_t* cu_q_lens,
+                                        const int32_t* chunk_offsets, const void* key_pool, const void* value_pool,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                        int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t num_blocks, int32_t causal, float scale,
+                                        pkv_dtype dtype, int32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,232 @@
+"""Python binding of libpagedkv.so (paged-KV attention for MI355X / gfx950).
+
+Argument marshalling only: every function checks tensor devices, dtypes and
+shapes, takes raw pointers and the current HIP stream, and calls the C entry
+point of the same name.  All computation happens in the HIP kernels.  The
+library is loaded on import; if it has not been built, the import fails
+loudly (there is no fallback).
+
+Tensors: pools are ``[num_blocks, 16, num_kv_heads, head_dim]`` (K and V
+separate, same dtype); block tables, context lengths, slot mappings and
+offsets are int32 device tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, 1, 2, 3, 4
+DTYPE_F32, DTYPE_BF16 = 0, 1
+FLAG_BAD_BLOCK, FLAG_BAD_SLOT, FLAG_BAD_LENGTH = 1, 2, 4
+BLOCK_SIZE = 16
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "pkv_status_string": (ctypes.c_char_p, [_i32]),
+    "pkv_slot_mapping": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_cache_write": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_paged_gather": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _vp, _vp]),
+    "pkv_decode_split_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                                     _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib.pkv_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise PagedKVError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("every tensor must be on the GPU")
+
+
+def _need_i32(*ts):
+    for t in ts:
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError("index tensors must be contiguous int32")
+
+
+def _pool_dims(key_pool: torch.Tensor, value_pool: torch.Tensor):
+    if key_pool.shape != value_pool.shape or key_pool.dtype != value_pool.dtype or key_pool.dim() != 4:
+        raise ValueError("key_pool and value_pool must both be [num_blocks, 16, num_kv_heads, head_dim], same dtype")
+    if not (key_pool.is_contiguous() and value_pool.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    nblk, bs, hkv, hd = key_pool.shape
+    return nblk, bs, hkv, hd
+
+
+def slot_mapping(block_tables: torch.Tensor, cu_new_lens: torch.Tensor, start_pos: torch.Tensor, max_new_len: int,
+                 num_blocks: int, err_flag: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 total: int | None = None) -> torch.Tensor:
+    """Slot (flat pool row) of each new token; see pkv_slot_mapping."""
+    _need_gpu(block_tables, cu_new_lens, start_pos, err_flag)
+    _need_i32(block_tables, cu_new_lens, start_pos, err_flag)
+    num_seqs = start_pos.shape[0]
+    if out is None:
+        if total is None:
+            total = int(cu_new_lens[-1].item())
+        out = torch.empty(total, dtype=torch.int32, device=block_tables.device)
+    _check(_lib.pkv_slot_mapping(_ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(cu_new_lens),
+                                 _ptr(start_pos), num_seqs, int(max_new_len), int(num_blocks), BLOCK_SIZE,
+                                 _ptr(err_flag), _stream(block_tables.device)), "pkv_slot_mapping")
+    return out
+
+
+def cache_write(key: torch.Tensor, value: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                slot_mapping: torch.Tensor, err_flag: torch.Tensor | None = None) -> None:
+    """Copy token rows key[t], value[t] into pool slots slot_mapping[t] (negative slots skipped)."""
+    _need_gpu(key, value, key_pool, value_pool, slot_mapping, err_flag)
+    _need_i32(slot_mapping, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    for t in (key, value):
+        if t.dtype != key_pool.dtype or t.dim() != 3 or tuple(t.shape[1:]) != (hkv, hd):
+            raise ValueError("key/value must be [T, num_kv_heads, head_dim] in the pool dtype")
+        if t.stride(2) != 1 or t.stride(1) != hd:
+            raise ValueError("key/value rows must be contiguous")
+    T = key.shape[0]
+    if value.shape[0] != T or slot_mapping.shape[0] < T:
+        raise ValueError("token counts differ")
+    _check(_lib.pkv_cache_write(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_pool),
+                                _ptr(value_pool), _ptr(slot_mapping), T, nblk, hkv, hd, bs,
+                                _dtype_code(key_pool), _ptr(err_flag), _stream(key.device)), "pkv_cache_write")
+
+
+def paged_gather(key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,
+                 lengths: torch.Tensor, cu_out: torch.Tensor, max_len: int, total: int,
+                 err_flag: torch.Tensor | None = None):
+    """Contiguous copies of each sequence's first lengths[s] rows (diagnostic of the block indexing)."""
+    _need_gpu(key_pool, value_pool, block_tables, lengths, cu_out, err_flag)
+    _need_i32(block_tables, lengths, cu_out, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    kout = torch.empty((total, hkv, hd), dtype=key_pool.dtype, device=key_pool.device)
+    vout = torch.empty_like(kout)
+    _check(_lib.pkv_paged_gather(_ptr(kout), _ptr(vout), _ptr(key_pool), _ptr(value_pool), _ptr(block_tables),
+                                 block_tables.shape[1], _ptr(lengths), _ptr(cu_out), lengths.shape[0], int(max_len),
+                                 nblk, hkv, hd, bs, _dtype_code(key_pool), _ptr(err_flag),
+                                 _stream(key_pool.device)), "pkv_paged_gather")
+    return kout, vout
+
+
+def decode_split_tokens(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                        max_blocks_per_seq: int) -> int:
+    return int(_lib.pkv_decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_blocks_per_seq: int, split_tokens: int = 0) -> int:
+    return int(_lib.pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                               split_tokens))
+
+
+def decode_workspace(query: torch.Tensor, num_kv_heads: int, max_blocks_per_seq: int,
+                     split_tokens: int = 0) -> torch.Tensor:
+    """Allocate a decode workspace for these shapes (a byte tensor on the query's device)."""
+    n = decode_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads, query.shape[2], max_blocks_per_seq,
+                               split_tokens)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=query.device)
+
+
+def paged_attn_decode(query: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                      workspace: torch.Tensor | None = None, split_tokens: int = 0,
+                      err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """One-token decode over the paged cache; see pkv_paged_attn_decode."""
+    _need_gpu(query, key_pool, value_pool, block_tables, context_lens, out, workspace, err_flag)
+    _need_i32(block_tables, context_lens, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != key_pool.dtype or not query.is_contiguous():
+        raise ValueError("query must be contiguous [num_seqs, num_q_heads, head_dim] in the pool dtype")
+    B, hq, _ = query.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((B, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (B, hq, hd):
+        raise ValueError("out must be contiguous [num_seqs, num_q_heads, head_dim]")
+    if workspace is None:
+        workspace = decode_workspace(query, hkv, block_tables.shape[1], split_tokens)
+    _check(_lib.pkv_paged_attn_decode(_ptr(out), _dtype_code(out), _ptr(query), _ptr(key_pool), _ptr(value_pool),
+                                      _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, hq, hkv, hd,
+                                      nblk, float(scale), _dtype_code(key_pool), int(split_tokens),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _ptr(err_flag), _stream(query.device)), "pkv_paged_attn_decode")
+    return out
+
+
+def paged_attn_prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk_offsets: torch.Tensor,
+                             key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,
+                             max_q_len: int, scale: float, causal: bool = True, out: torch.Tensor | None = None,
+                             out_dtype: torch.dtype = torch.float32,
+                             err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunked-prefill attention over the paged cache; see pkv_paged_attn_prefill_chunk."""
+    _need_gpu(query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables, out, err_flag)
+    _need_i32(cu_q_lens, chunk_offsets, block_tables, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != key_pool.dtype or not query.is_contiguous():
+        raise ValueError("query must be contiguous [rows, num_q_heads, head_dim] in the pool dtype")
+    rows, hq, _ = query.shape
+    num_seqs = chunk_offsets.shape[0]
+    if cu_q_lens.shape[0] != num_seqs + 1 or block_tables.shape[0] != num_seqs:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((rows, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (rows, hq, hd):
+        raise ValueError("out must be contiguous [rows, num_q_heads, head_dim]")
+    _check(_lib.pkv_paged_attn_prefill_chunk(_ptr(out), _dtype_code(out), _ptr(query), _ptr(cu_q_lens),
+                                             _ptr(chunk_offsets), _ptr(key_pool), _ptr(value_pool),
+                                             _ptr(block_tables), block_tables.shape[1], num_seqs, int(max_q_len), hq,
+                                             hkv, hd, nblk, int(bool(causal)), float(scale), _dtype_code(key_pool),
+                                             _ptr(err_flag), _stream(query.device)),
+           "pkv_paged_attn_prefill_chunk")
+    return out

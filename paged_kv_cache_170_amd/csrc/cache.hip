@@ -1,0 +1,202 @@
+// Slot mapping, slot-mapped cache write and the paged gather diagnostic.
+//
+// Slot mapping follows the block-table definition of "第2章:推理引擎核心技术" (aiinfra.vidrealm.tech)
+// §1.2 and the PagedAttention section of "Phase 17 · 04 — vLLM serving internals": the physical
+// block of position p is the table entry of logical block p / 16, its row inside the block is
+// p % 16.  The write stores new tokens' K/V rows in those slots ("Chunked Prefill", Ultralytics,
+// section on prefill and decode); the gather reproduces the figure 按块表取 K of "C13 推理 · 第2课"
+// (rows of the pool taken through the table, in logical order).
+#include "common.hpp"
+
+namespace pkv {
+
+// One thread per new token.  grid = (ceil(max_new_len / 256), num_seqs).
+template <bool CHECK>
+__global__ __launch_bounds__(256) void slot_mapping_kernel(int32_t* __restrict__ slots,
+                                                           const int32_t* __restrict__ block_tables, int max_blocks,
+                                                           const int32_t* __restrict__ cu_new_lens,
+                                                           const int32_t* __restrict__ start_pos, int num_blocks,
+                                                           int32_t* err_flag) {
+  const int s = blockIdx.y;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lo = cu_new_lens[s];
+  const int n = cu_new_lens[s + 1] - lo;
+  if (i >= n) return;
+  const int p = start_pos[s] + i;
+  const int j = p >> 4;
+  int slot = -1;
+  if (p >= 0 && j < max_blocks) {
+    const int b = load_block_id<CHECK>(block_tables + static_cast<int64_t>(s) * max_blocks, j, num_blocks, err_flag);
+    if (b >= 0) slot = b * kBlockSize + (p & (kBlockSize - 1));
+  } else if (CHECK) {
+    atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+  }
+  slots[lo + i] = slot;
+}
+
+// Row copy: each thread moves one VEC-byte piece of one token's K row and V row.  Rows are
+// `row_bytes` long; VEC divides row_bytes and the alignment of every address.
+template <int VEC, bool CHECK>
+__global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict__ key, const char* __restrict__ value,
+                                                          int64_t key_stride_bytes, int64_t value_stride_bytes,
+                                                          char* __restrict__ key_pool, char* __restrict__ value_pool,
+                                                          const int32_t* __restrict__ slots, int num_tokens,
+                                                          int row_bytes, int64_t num_slots, int32_t* err_flag) {
+  const int pieces = row_bytes / VEC;
+  const int64_t total = static_cast<int64_t>(num_tokens) * pieces;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int t = static_cast<int>(i / pieces);
+    const int c = static_cast<int>(i - static_cast<int64_t>(t) * pieces);
+    const int slot = slots[t];
+    if (slot < 0) continue;
+    if (CHECK && slot >= num_slots) {
+      if (c == 0) atomicOr(err_flag, PKV_FLAG_BAD_SLOT);
+      continue;
+    }
+    const int64_t dst = static_cast<int64_t>(slot) * row_bytes + static_cast<int64_t>(c) * VEC;
+    const char* ks = key + t * key_stride_bytes + c * VEC;
+    const char* vs = value + t * value_stride_bytes + c * VEC;
+    if constexpr (VEC == 16) {
+      st16(key_pool + dst, ld16(ks));
+      st16(value_pool + dst, ld16(vs));
+    } else if constexpr (VEC == 4) {
+      *reinterpret_cast<uint32_t*>(key_pool + dst) = *reinterpret_cast<const uint32_t*>(ks);
+      *reinterpret_cast<uint32_t*>(value_pool + dst) = *reinterpret_cast<const uint32_t*>(vs);
+    } else {
+      *reinterpret_cast<uint16_t*>(key_pool + dst) = *reinterpret_cast<const uint16_t*>(ks);
+      *reinterpret_cast<uint16_t*>(value_pool + dst) = *reinterpret_cast<const uint16_t*>(vs);
+    }
+  }
+}
+
+// Gather: grid = (ceil(max_len * pieces / 256), num_seqs); 16-byte pieces of whole token rows.
+template <bool CHECK>
+__global__ __launch_bounds__(256) void paged_gather_kernel(char* __restrict__ key_out, char* __restrict__ value_out,
+                                                           const char* __restrict__ key_pool,
+                                                           const char* __restrict__ value_pool,
+                                                           const int32_t* __restrict__ block_tables, int max_blocks,
+                                                           const int32_t* __restrict__ lengths,
+                                                           const int32_t* __restrict__ cu_out, int num_blocks,
+                                                           int num_kv_heads, int head_dim, int elem_bytes,
+                                                           int32_t* err_flag) {
+  const int row_bytes = num_kv_heads * head_dim * elem_bytes;
+  const int s = blockIdx.y;
+  const int pieces = row_bytes / 16;
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  const int t = static_cast<int>(i / pieces);
+  const int c = static_cast<int>(i - static_cast<int64_t>(t) * pieces);
+  const int len = lengths[s];
+  if (t >= len) return;
+  if (CHECK && len > max_blocks * kBlockSize) {
+    if (t == 0 && c == 0) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+    return;
+  }
+  const int b = load_block_id<CHECK>(block_tables + static_cast<int64_t>(s) * max_blocks, t >> 4, num_blocks,
+                                     err_flag);
+  if (b < 0) return;
+  // Same row arithmetic as the attention kernels (KV head 0 starts the whole token row).
+  const int64_t src = pool_row_offset(b, t & (kBlockSize - 1), num_kv_heads, 0, head_dim) * elem_bytes + c * 16;
+  const int64_t dst = (static_cast<int64_t>(cu_out[s]) + t) * row_bytes + c * 16;
+  st16(key_out + dst, ld16(key_pool + src));
+  st16(value_out + dst, ld16(value_pool + src));
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+namespace {
+int dtype_bytes(pkv_dtype d) { return d == PKV_DTYPE_F32 ? 4 : (d == PKV_DTYPE_BF16 ? 2 : 0); }
+bool head_dim_ok(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+}  // namespace
+
+extern "C" pkv_status pkv_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* cu_new_lens, const int32_t* start_pos, int32_t num_seqs,
+                                       int32_t max_new_len, int32_t num_blocks, int32_t block_size,
+                                       int32_t* err_flag, void* stream) {
+  if (num_seqs < 0 || max_new_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0) return PKV_ERR_INVALID_ARG;
+  if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_new_len == 0) return PKV_OK;
+  if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;  // grid y limit
+  if (!slot_mapping || !block_tables || !cu_new_lens || !start_pos || max_blocks_per_seq == 0)
+    return PKV_ERR_INVALID_ARG;
+  dim3 grid((max_new_len + 255) / 256, num_seqs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (err_flag)
+    hipLaunchKernelGGL(slot_mapping_kernel<true>, grid, dim3(256), 0, st, slot_mapping, block_tables,
+                       max_blocks_per_seq, cu_new_lens, start_pos, num_blocks, err_flag);
+  else
+    hipLaunchKernelGGL(slot_mapping_kernel<false>, grid, dim3(256), 0, st, slot_mapping, block_tables,
+                       max_blocks_per_seq, cu_new_lens, start_pos, num_blocks, err_flag);
+  return pkv_host::launch_status();
+}
+
+extern "C" pkv_status pkv_cache_write(const void* key, const void* value, int64_t key_tok_stride,
+                                      int64_t value_tok_stride, void* key_pool, void* value_pool,
+                                      const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                                      int32_t* err_flag, void* stream) {
+  const int e = dtype_bytes(dtype);
+  if (e == 0 || block_size != kBlockSize || !head_dim_ok(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (key_tok_stride < row_elems || value_tok_stride < row_elems) return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_pool || !value_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  const int row_bytes = static_cast<int>(row_elems * e);
+  const int64_t ks = key_tok_stride * e, vs = value_tok_stride * e;
+  auto aligned = [](const void* p, int a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  const bool a16 = aligned(key, 16) && aligned(value, 16) && aligned(key_pool, 16) && aligned(value_pool, 16) &&
+                   ks % 16 == 0 && vs % 16 == 0;
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * kBlockSize;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int vec = a16 ? 16 : e;
+  const int64_t total = static_cast<int64_t>(num_tokens) * (row_bytes / vec);
+  const int64_t want = (total + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+#define PKV_LAUNCH_WRITE(V, C)                                                                                   \
+  hipLaunchKernelGGL((cache_write_kernel<V, C>), dim3(blocks), dim3(256), 0, st, static_cast<const char*>(key),  \
+                     static_cast<const char*>(value), ks, vs, static_cast<char*>(key_pool),                      \
+                     static_cast<char*>(value_pool), slot_mapping, num_tokens, row_bytes, num_slots, err_flag)
+  if (vec == 16) {
+    if (err_flag) PKV_LAUNCH_WRITE(16, true); else PKV_LAUNCH_WRITE(16, false);
+  } else if (vec == 4) {
+    if (err_flag) PKV_LAUNCH_WRITE(4, true); else PKV_LAUNCH_WRITE(4, false);
+  } else {
+    if (err_flag) PKV_LAUNCH_WRITE(2, true); else PKV_LAUNCH_WRITE(2, false);
+  }
+#undef PKV_LAUNCH_WRITE
+  return pkv_host::launch_status();
+}
+
+extern "C" pkv_status pkv_paged_gather(void* key_out, void* value_out, const void* key_pool, const void* value_pool,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* lengths, const int32_t* cu_out, int32_t num_seqs,
+                                       int32_t max_len, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, pkv_dtype dtype, int32_t* err_flag, void* stream) {
+  const int e = dtype_bytes(dtype);
+  if (e == 0 || block_size != kBlockSize || !head_dim_ok(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_len < 0 || num_blocks < 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_len == 0) return PKV_OK;
+  if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;  // grid y limit
+  if (!key_out || !value_out || !key_pool || !value_pool || !block_tables || !lengths || !cu_out ||
+      max_blocks_per_seq == 0)
+    return PKV_ERR_INVALID_ARG;
+  const int row_bytes = num_kv_heads * head_dim * e;
+  const int64_t threads = static_cast<int64_t>(max_len) * (row_bytes / 16);
+  dim3 grid(static_cast<unsigned>((threads + 255) / 256), num_seqs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (err_flag)
+    hipLaunchKernelGGL(paged_gather_kernel<true>, grid, dim3(256), 0, st, static_cast<char*>(key_out),
+                       static_cast<char*>(value_out), static_cast<const char*>(key_pool),
+                       static_cast<const char*>(value_pool), block_tables, max_blocks_per_seq, lengths, cu_out,
+                       num_blocks, num_kv_heads, head_dim, e, err_flag);
+  else
+    hipLaunchKernelGGL(paged_gather_kernel<false>, grid, dim3(256), 0, st, static_cast<char*>(key_out),
+                       static_cast<char*>(value_out), static_cast<const char*>(key_pool),
+                       static_cast<const char*>(value_pool), block_tables, max_blocks_per_seq, lengths, cu_out,
+                       num_blocks, num_kv_heads, head_dim, e, err_flag);
+  return pkv_host::launch_status();
+}

@@ -1,0 +1,80 @@
+// Shared device/host helpers for the paged-KV kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstddef>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+
+constexpr int kBlockSize = 16;  // tokens per physical KV block
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------------------------
+// Pool addressing.  A pool is [num_blocks, 16, num_kv_heads, head_dim]; a token's row for one KV
+// head starts at ((block * 16 + offset) * num_kv_heads + kv_head) * head_dim elements.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int64_t pool_row_offset(int block, int offset, int num_kv_heads, int kv_head,
+                                                   int head_dim) {
+  return ((static_cast<int64_t>(block) * kBlockSize + offset) * num_kv_heads + kv_head) *
+         static_cast<int64_t>(head_dim);
+}
+
+// Reads the physical block of logical block `j` of a sequence.  In checked mode an id outside
+// [0, num_blocks) sets PKV_FLAG_BAD_BLOCK and yields -1 so the caller skips the page.
+template <bool CHECK>
+__device__ __forceinline__ int load_block_id(const int32_t* table_row, int j, int num_blocks, int32_t* err_flag) {
+  int b = table_row[j];
+  if (CHECK) {
+    if (b < 0 || b >= num_blocks) {
+      atomicOr(err_flag, PKV_FLAG_BAD_BLOCK);
+      return -1;
+    }
+  }
+  return b;
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // round to nearest even
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS transpose read of four 16-bit elements.  Within each group of 16 lanes, lane i receives
+// element (i % 4) of the 8-byte rows addressed by lanes 4e + i/4 (e = 0..3) of its group.
+// `lds_ptr` must point into __shared__ memory and be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* lds_ptr) {
+  typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+  shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lds_ptr));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+}  // namespace pkv
+
+// Host helpers (defined in status.hip).
+namespace pkv_host {
+int cu_count();                 // compute units of the current device, cached per device
+pkv_status launch_status();     // PKV_OK or PKV_ERR_HIP from hipGetLastError()
+}  // namespace pkv_host

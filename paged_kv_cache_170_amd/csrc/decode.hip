@@ -1,0 +1,516 @@
+// One-token paged decode with split-KV partition and log-sum-exp combine.
+//
+// What is computed: for each sequence s and query head h, softmax attention of q[s][h] over the
+// sequence's cached positions 0 .. ctx_s - 1 of KV head h / G ("Chunked Prefill", Ultralytics,
+// section on prefill and decode: decode reads the whole cache every step).  The pages' paged
+// kernel ("第2章:推理引擎核心技术", §1.4) walks the request's pages through its table and keeps an
+// online softmax; here the walk is split over workgroups and the partial states are merged.
+//
+// Design (gfx950, wave64):
+//   * grid (split, kv_head, seq); a workgroup of 4 waves owns `split_tokens` positions of one
+//     (sequence, KV head) and serves all G query heads of that group from each loaded page.
+//   * a wave step covers 32 positions = two 16-token blocks.  K is loaded straight into MFMA
+//     operand registers; S^T = K Q^T uses v_mfma_f32_16x16x32_bf16 with the 16 MFMA columns
+//     holding the G query heads (zero-padded).  V rows are staged in LDS in their natural layout
+//     and read back transposed with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T.
+//   * the online softmax runs in the log2 domain on the MFMA accumulator layout; the 4 waves'
+//     states merge in LDS, and a split's (o, m, l) goes to the workspace unless the sequence
+//     fits one split, in which case the normalised row is written directly.
+//   * fp32 pools take a plain VALU kernel with the same split/merge structure.
+#include <cstdlib>
+#include <cmath>
+
+#include "common.hpp"
+
+namespace pkv {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kMaxGroup = 16;
+
+template <int HD>
+struct DecCfg {
+  static constexpr int KK = HD / 32;          // k-steps of S^T = K Q^T over head_dim
+  static constexpr int MT = HD / 16;          // 16-row tiles of O^T
+  static constexpr int VPITCH = HD * 2 + 32;  // bytes per staged V row (keeps transposed reads conflict-free)
+  static constexpr int LPR = HD / 8;          // lanes per V row in a 16-byte-per-lane load
+  static constexpr int RPL = kWave / LPR;     // V rows per wave-wide load
+  static constexpr int VLD = kBlockSize / RPL;  // wave-wide loads per block
+  static constexpr int STAGE = 2 * kBlockSize * VPITCH;  // bytes per wave
+  static constexpr int COMB = kMaxGroup * HD * 4;        // bytes per wave for the merge
+  static constexpr int BODY = (STAGE > COMB ? STAGE : COMB) * kDecWaves;
+  static constexpr int LDS = BODY + kDecWaves * kMaxGroup * 2 * 4;
+};
+
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool bf16) {
+  if (bf16)
+    static_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+  else
+    static_cast<float*>(out)[idx] = v;
+}
+
+// Merges the per-wave states held in LDS and writes either the final rows or the split partial.
+template <int HD>
+__device__ __forceinline__ void merge_waves(const float* comb_o, const float* comb_ml, int group, int s, int g,
+                                            int split, int nsplit, int max_splits, int num_q_heads, float* ws_o,
+                                            float* ws_ml, void* out, bool out_bf16) {
+  for (int i = threadIdx.x; i < group * HD; i += kDecThreads) {
+    const int hn = i / HD, d = i - hn * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, comb_ml[(w * kMaxGroup + hn) * 2]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = comb_ml[(w * kMaxGroup + hn) * 2];
+      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+      O += f * comb_o[(w * kMaxGroup + hn) * HD + d];
+      L += f * comb_ml[(w * kMaxGroup + hn) * 2 + 1];
+    }
+    const int h = g * group + hn;
+    const int64_t row = static_cast<int64_t>(s) * num_q_heads + h;
+    if (nsplit == 1) {
+      store_out(out, row * HD + d, L > 0.f ? O / L : 0.f, out_bf16);
+    } else {
+      const int64_t part = row * max_splits + split;
+      ws_o[part * HD + d] = O;
+      if (d == 0) {
+        ws_ml[part * 2] = M;
+        ws_ml[part * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Clamps a context length to the table; flags it in checked mode.
+template <bool CHECK>
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int32_t* err_flag, bool report) {
+  if (ctx < 0 || ctx > max_blocks * kBlockSize) {
+    if (CHECK && report) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+    return ctx < 0 ? 0 : max_blocks * kBlockSize;
+  }
+  return ctx;
+}
+
+template <int HD, bool CHECK>
+__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
+    const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_pool, const uint16_t* __restrict__ value_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
+    int num_q_heads, int num_kv_heads, int group, int num_blocks, float scale_log2, int split_tokens, int max_splits,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ out, int out_bf16, int32_t* err_flag) {
+  using C = DecCfg<HD>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int ctx = clamp_ctx<CHECK>(context_lens[s], max_blocks, err_flag, split == 0 && g == 0 && threadIdx.x == 0);
+  const int nsplit = (ctx + split_tokens - 1) / split_tokens;
+  if (ctx == 0) {
+    if (split != 0) return;
+    for (int i = threadIdx.x; i < group * HD; i += kDecThreads)
+      store_out(out, (static_cast<int64_t>(s) * num_q_heads + g * group) * HD + i, 0.f, out_bf16);
+    return;
+  }
+  if (split >= nsplit) return;
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = lane & 15, c = lane >> 4;
+  const int tok0 = split * split_tokens;
+  const int tok_end = min(tok0 + split_tokens, ctx);
+  const int32_t* table = block_tables + static_cast<int64_t>(s) * max_blocks;
+
+  // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.
+  bf16x8 qf[C::KK];
+  {
+    const bool live = n < group;
+    const uint16_t* qrow = query + (static_cast<int64_t>(s) * num_q_heads + g * group + (live ? n : 0)) * HD + 8 * c;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  floatx4 acc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t* vstage = reinterpret_cast<uint16_t*>(smem + wave * C::STAGE);
+  constexpr int VP = C::VPITCH / 2;  // pitch in elements
+  const int units = (tok_end - tok0 + 31) / 32;
+
+  for (int u = wave; u < units; u += kDecWaves) {
+    const int t0 = tok0 + 32 * u;
+    const int j0 = t0 / kBlockSize;
+    const bool has1 = t0 + kBlockSize < ctx;
+    const int b0 = load_block_id<CHECK>(table, j0, num_blocks, err_flag);
+    const int b1 = has1 ? load_block_id<CHECK>(table, j0 + 1, num_blocks, err_flag) : -1;
+
+    // Issue every load of the step before any use.
+    uint4 kf[2][C::KK];
+    uint4 vf[2][C::VLD];
+    const int vrow_base = lane / C::LPR, vcol = (lane % C::LPR) * 8;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const int b = pg ? b1 : b0;
+      if (b >= 0) {
+        const uint16_t* kb = key_pool + pool_row_offset(b, n, num_kv_heads, g, HD) + 8 * c;
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) kf[pg][kk] = ld16(kb + 32 * kk);
+#pragma unroll
+        for (int i = 0; i < C::VLD; ++i)
+          vf[pg][i] = ld16(value_pool + pool_row_offset(b, i * C::RPL + vrow_base, num_kv_heads, g, HD) + vcol);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) kf[pg][kk] = uint4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < C::VLD; ++i) vf[pg][i] = uint4{0, 0, 0, 0};
+      }
+    }
+
+    // S^T = K Q^T for both blocks: lane (n, c) gets head n, tokens 4c .. 4c+3 of each block.
+    floatx4 sacc[2];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      sacc[pg] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk)
+        sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[pg][kk]), qf[kk], sacc[pg], 0, 0, 0);
+    }
+
+    // Stage V (rows at or past ctx become zero so that stale slots never reach the MFMA).
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int i = 0; i < C::VLD; ++i) {
+        const int row = i * C::RPL + vrow_base;
+        const uint4 v = (t0 + pg * kBlockSize + row < ctx) ? vf[pg][i] : uint4{0, 0, 0, 0};
+        st16(vstage + (pg * kBlockSize + row) * VP + vcol, v);
+      }
+
+    // Online softmax over the 32 positions of this step (log2 domain).
+    float x[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const bool blk_ok = (pg ? b1 : b0) >= 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = t0 + pg * kBlockSize + 4 * c + j;
+        const float v = (blk_ok && tok < ctx) ? sacc[pg][j] * scale_log2 : -INFINITY;
+        x[pg * 4 + j] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(x[e] - m_use);
+      psum += p;
+      pb[e] = static_cast<__bf16>(p);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) acc[mt] *= alpha;
+
+    // The staged rows are read back by this wave only; keep the compiler from moving reads up.
+    __asm__ volatile("" ::: "memory");
+
+    // O^T += V^T P^T.  A operand: lane (n, c) needs V[token 4c+e][d = 16mt + n] of both blocks.
+    const uint16_t* r0 = vstage + (4 * c + (n >> 2)) * VP + 4 * (n & 3);
+    const uint16_t* r1 = r0 + kBlockSize * VP;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt) {
+      const bf16x8 a = concat(lds_read_tr16(r0 + 16 * mt), lds_read_tr16(r1 + 16 * mt));
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[mt], 0, 0, 0);
+    }
+    __asm__ volatile("" ::: "memory");
+  }
+
+  // Normaliser of head n: sum the four lane groups.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  __syncthreads();  // every wave is done with its staging area
+  float* comb_o = reinterpret_cast<float*>(smem);
+  float* comb_ml = reinterpret_cast<float*>(smem + C::BODY);
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+    *reinterpret_cast<floatx4*>(comb_o + (wave * kMaxGroup + n) * HD + 16 * mt + 4 * c) = acc[mt];
+  if (c == 0) {
+    comb_ml[(wave * kMaxGroup + n) * 2] = m_run;
+    comb_ml[(wave * kMaxGroup + n) * 2 + 1] = l_run;
+  }
+  __syncthreads();
+  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16);
+}
+
+// fp32 pools: VALU kernel.  A wave step covers 32 positions; lanes 0-31 and 32-63 each take one
+// position and half of head_dim for the scores, then lanes span head_dim for P V.
+template <int HD, bool CHECK>
+__global__ __launch_bounds__(kDecThreads) void decode_f32_kernel(
+    const float* __restrict__ query, const float* __restrict__ key_pool, const float* __restrict__ value_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
+    int num_q_heads, int num_kv_heads, int group, int num_blocks, float scale_log2, int split_tokens, int max_splits,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ out, int out_bf16, int32_t* err_flag) {
+  constexpr int DPL = HD / kWave;  // head_dim elements per lane in P V
+  constexpr int HALF = HD / 2;
+  constexpr int COMB = kMaxGroup * HD * 4 * kDecWaves;
+  __shared__ __attribute__((aligned(16))) char smem[COMB + kDecWaves * kMaxGroup * 2 * 4 + kMaxGroup * HD * 4];
+  float* q_lds = reinterpret_cast<float*>(smem + COMB + kDecWaves * kMaxGroup * 2 * 4);
+
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int ctx = clamp_ctx<CHECK>(context_lens[s], max_blocks, err_flag, split == 0 && g == 0 && threadIdx.x == 0);
+  const int nsplit = (ctx + split_tokens - 1) / split_tokens;
+  if (ctx == 0) {
+    if (split != 0) return;
+    for (int i = threadIdx.x; i < group * HD; i += kDecThreads)
+      store_out(out, (static_cast<int64_t>(s) * num_q_heads + g * group) * HD + i, 0.f, out_bf16);
+    return;
+  }
+  if (split >= nsplit) return;
+  for (int i = threadIdx.x; i < group * HD; i += kDecThreads)
+    q_lds[i] = query[(static_cast<int64_t>(s) * num_q_heads + g * group) * HD + i];
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int tl = lane & 31, half = lane >> 5;
+  const int tok0 = split * split_tokens;
+  const int tok_end = min(tok0 + split_tokens, ctx);
+  const int32_t* table = block_tables + static_cast<int64_t>(s) * max_blocks;
+
+  float m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][DPL];
+#pragma unroll
+  for (int hn = 0; hn < kMaxGroup; ++hn) {
+    m_run[hn] = -INFINITY;
+    l_run[hn] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[hn][k] = 0.f;
+  }
+
+  const int units = (tok_end - tok0 + 31) / 32;
+  for (int u = wave; u < units; u += kDecWaves) {
+    const int t0 = tok0 + 32 * u;
+    const int j0 = t0 / kBlockSize;
+    const bool has1 = t0 + kBlockSize < ctx;
+    const int b0 = load_block_id<CHECK>(table, j0, num_blocks, err_flag);
+    const int b1 = has1 ? load_block_id<CHECK>(table, j0 + 1, num_blocks, err_flag) : -1;
+    const int tok = t0 + tl;
+    const int bt = tl < kBlockSize ? b0 : b1;
+    const bool valid = tok < ctx && bt >= 0;
+
+    float sc[kMaxGroup];
+#pragma unroll
+    for (int hn = 0; hn < kMaxGroup; ++hn) sc[hn] = 0.f;
+    if (valid) {
+      const float* krow = key_pool + pool_row_offset(bt, tok % kBlockSize, num_kv_heads, g, HD) + half * HALF;
+      for (int d = 0; d < HALF; d += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(krow + d);
+#pragma unroll
+        for (int hn = 0; hn < kMaxGroup; ++hn) {
+          if (hn < group) {
+            const float* qv = q_lds + hn * HD + half * HALF + d;
+            sc[hn] += qv[0] * kv.x + qv[1] * kv.y + qv[2] * kv.z + qv[3] * kv.w;
+          }
+        }
+      }
+    }
+    float p[kMaxGroup];
+#pragma unroll
+    for (int hn = 0; hn < kMaxGroup; ++hn) {
+      if (hn >= group) continue;
+      const float full = sc[hn] + __shfl_xor(sc[hn], 32);
+      const float xv = valid ? full * scale_log2 : -INFINITY;
+      float mx = xv;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_new = fmaxf(m_run[hn], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[hn] - m_use);
+      const float pv = fast_exp2(xv - m_use);
+      float ps = pv;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) ps += __shfl_xor(ps, off);
+      l_run[hn] = l_run[hn] * alpha + ps;
+      m_run[hn] = m_new;
+      p[hn] = pv;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[hn][k] *= alpha;
+    }
+    const int nt = min(32, ctx - t0);
+    for (int tt = 0; tt < nt; ++tt) {
+      const int b = tt < kBlockSize ? b0 : b1;
+      if (b < 0) continue;
+      const float* vrow = value_pool + pool_row_offset(b, (t0 + tt) % kBlockSize, num_kv_heads, g, HD);
+      float vv[DPL];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) vv[k] = vrow[lane + kWave * k];
+#pragma unroll
+      for (int hn = 0; hn < kMaxGroup; ++hn) {
+        if (hn >= group) continue;
+        const float w = __shfl(p[hn], tt);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) o[hn][k] += w * vv[k];
+      }
+    }
+  }
+
+  __syncthreads();
+  float* comb_o = reinterpret_cast<float*>(smem);
+  float* comb_ml = reinterpret_cast<float*>(smem + COMB);
+#pragma unroll
+  for (int hn = 0; hn < kMaxGroup; ++hn) {
+    if (hn >= group) continue;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) comb_o[(wave * kMaxGroup + hn) * HD + lane + kWave * k] = o[hn][k];
+    if (lane == 0) {
+      comb_ml[(wave * kMaxGroup + hn) * 2] = m_run[hn];
+      comb_ml[(wave * kMaxGroup + hn) * 2 + 1] = l_run[hn];
+    }
+  }
+  __syncthreads();
+  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16);
+}
+
+// Log-sum-exp merge of split partials: grid (num_q_heads, num_seqs), one thread per head_dim element.
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ ws_o,
+                                                            const float* __restrict__ ws_ml,
+                                                            const int32_t* __restrict__ context_lens, int max_blocks,
+                                                            int num_q_heads, int head_dim, int split_tokens,
+                                                            int max_splits, void* __restrict__ out, int out_bf16) {
+  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+  int ctx = context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > max_blocks * kBlockSize ? max_blocks * kBlockSize : ctx);
+  const int nsplit = (ctx + split_tokens - 1) / split_tokens;
+  if (nsplit <= 1 || d >= head_dim) return;
+  const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_splits;
+  float M = -INFINITY;
+  for (int p = 0; p < nsplit; ++p) M = fmaxf(M, ws_ml[(base + p) * 2]);
+  float O = 0.f, L = 0.f;
+  for (int p = 0; p < nsplit; ++p) {
+    const float mp = ws_ml[(base + p) * 2];
+    const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
+    O += f * ws_o[(base + p) * head_dim + d];
+    L += f * ws_ml[(base + p) * 2 + 1];
+  }
+  store_out(out, (static_cast<int64_t>(s) * num_q_heads + h) * head_dim + d, L > 0.f ? O / L : 0.f, out_bf16 != 0);
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+namespace {
+
+int env_split_tokens() {
+  static const int v = [] {
+    const char* e = std::getenv("PKV_SPLIT_TOKENS");
+    if (!e) return 0;
+    const int x = std::atoi(e);
+    return (x > 0 && x % 128 == 0) ? x : 0;
+  }();
+  return v;
+}
+
+bool shapes_ok(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t hd, int32_t max_blocks) {
+  return num_seqs >= 0 && hq > 0 && hkv > 0 && hq % hkv == 0 && hq / hkv <= kMaxGroup &&
+         (hd == 64 || hd == 128 || hd == 256) && max_blocks > 0;
+}
+
+int32_t resolve_split(int32_t requested, int32_t num_seqs, int32_t hq, int32_t hkv, int32_t hd, int32_t max_blocks) {
+  if (requested > 0) return requested;
+  return pkv_decode_split_tokens(num_seqs, hq, hkv, hd, max_blocks);
+}
+
+size_t partial_bytes(int32_t num_seqs, int32_t hq, int32_t hd, int32_t max_splits) {
+  const size_t rows = static_cast<size_t>(num_seqs) * hq * max_splits;
+  const size_t o = (rows * hd * 4 + 255) / 256 * 256;
+  return o + rows * 2 * 4;
+}
+
+}  // namespace
+
+extern "C" int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t max_blocks_per_seq) {
+  if (const int e = env_split_tokens()) return e;
+  if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 512;
+  const int64_t max_ctx = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
+  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  // Prefer long splits (fewer partials) while the grid still offers several workgroups per CU.
+  if (pairs * ((max_ctx + 511) / 512) >= 1024) return 512;
+  if (pairs * ((max_ctx + 255) / 256) >= 512) return 256;
+  return 128;
+}
+
+extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t max_blocks_per_seq, int32_t split_tokens) {
+  if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 0;
+  if (split_tokens < 0 || split_tokens % 128 != 0) return 0;
+  const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+  const int64_t max_splits = (static_cast<int64_t>(max_blocks_per_seq) * kBlockSize + S - 1) / S;
+  if (max_splits <= 1) return 0;
+  return partial_bytes(num_seqs, num_q_heads, head_dim, static_cast<int32_t>(max_splits));
+}
+
+extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                            const void* value_pool, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t num_blocks, float scale, pkv_dtype dtype,
+                                            int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                            int32_t* err_flag, void* stream) {
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || !std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return PKV_ERR_UNSUPPORTED;
+  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid y/z limits
+  if (!out || !query || !key_pool || !value_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+  const int64_t max_splits64 = (static_cast<int64_t>(max_blocks_per_seq) * kBlockSize + S - 1) / S;
+  if (max_splits64 > 65535) return PKV_ERR_UNSUPPORTED;
+  const int max_splits = static_cast<int>(max_splits64);
+  const size_t need = max_splits > 1 ? partial_bytes(num_seqs, num_q_heads, head_dim, max_splits) : 0;
+  if (workspace_bytes < need || (need > 0 && !workspace)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  float* ws_o = static_cast<float*>(workspace);
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * max_splits;
+  float* ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + (rows * head_dim * 4 + 255) / 256 * 256)
+                      : nullptr;
+  const int group = num_q_heads / num_kv_heads;
+  const float scale_log2 = scale * kLog2e;
+  const int ob = out_dtype == PKV_DTYPE_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dim3 grid(max_splits, num_kv_heads, num_seqs);
+
+#define PKV_DEC(KERNEL, T, HD, CHECK)                                                                              \
+  hipLaunchKernelGGL((KERNEL<HD, CHECK>), grid, dim3(kDecThreads), 0, st, static_cast<const T*>(query),            \
+                     static_cast<const T*>(key_pool), static_cast<const T*>(value_pool), block_tables,             \
+                     max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads, group, num_blocks, scale_log2, S, \
+                     max_splits, ws_o, ws_ml, out, ob, err_flag)
+#define PKV_DEC_HD(KERNEL, T, CHECK)                 \
+  switch (head_dim) {                                \
+    case 64: PKV_DEC(KERNEL, T, 64, CHECK); break;   \
+    case 128: PKV_DEC(KERNEL, T, 128, CHECK); break; \
+    default: PKV_DEC(KERNEL, T, 256, CHECK); break;  \
+  }
+  if (dtype == PKV_DTYPE_BF16) {
+    if (err_flag) { PKV_DEC_HD(decode_bf16_kernel, uint16_t, true) } else { PKV_DEC_HD(decode_bf16_kernel, uint16_t, false) }
+  } else {
+    if (err_flag) { PKV_DEC_HD(decode_f32_kernel, float, true) } else { PKV_DEC_HD(decode_f32_kernel, float, false) }
+  }
+#undef PKV_DEC_HD
+#undef PKV_DEC
+  if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+  if (max_splits > 1) {
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(num_q_heads, num_seqs), dim3(head_dim), 0, st, ws_o, ws_ml,
+                       context_lens, max_blocks_per_seq, num_q_heads, head_dim, S, max_splits, out, ob);
+    return pkv_host::launch_status();
+  }
+  return PKV_OK;
+}

@@ -1,0 +1,266 @@
+// Chunked-prefill attention over the paged cache (bf16 MFMA, fp32 accumulation).
+//
+// What is computed ("Chunked Prefill", Ultralytics, section on how chunked prefill works, and its
+// PyTorch example): a chunk row at absolute position P attends to every cached key at a position
+// <= P (causal) — the earlier chunks and its own chunk, which the cache write stored first — so
+// the chunked result equals one-pass causal prefill.  Non-causal rows see the whole chunk end.
+//
+// Design (gfx950, wave64):
+//   * 1-D grid of (sequence, KV head, query head in group, 128-row query tile) work items; the
+//     workgroup id is remapped so that each XCD (workgroups are dealt round-robin over the 8 XCDs)
+//     gets a contiguous run of items, i.e. the query heads of one KV head, which then share that
+//     KV head's K/V stream in the XCD's L2.
+//   * 4 waves x 32 query rows.  Key tiles of 64 positions (4 blocks) are gathered through the
+//     block table into LDS (register prefetch of the next tile overlaps the current tile's math).
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows in registers);
+//     the accumulator layout gives each lane 16 keys of one query, so the row max needs one
+//     cross-lane step.  The causal mask is an absolute-position compare.
+//   * P stays in registers and is exactly the B operand of O^T = V^T P^T; V^T comes from the
+//     natural-layout V tile through ds_read_b64_tr_b16.
+#include <cmath>
+
+#include "common.hpp"
+
+namespace pkv {
+
+constexpr int kPreWaves = 4;
+constexpr int kPreThreads = kPreWaves * kWave;
+constexpr int kPreRows = 32;                        // query rows per wave
+constexpr int kPreTile = kPreWaves * kPreRows;      // query rows per workgroup
+constexpr int kKeyTile = 64;                        // key positions per LDS tile
+
+template <int HD>
+struct PreCfg {
+  static constexpr int KS = HD / 16;           // k-steps of S^T over head_dim
+  static constexpr int MD = HD / 32;           // 32-row tiles of O^T
+  static constexpr int KPITCH = HD * 2 + 16;   // LDS bytes per K row
+  static constexpr int VPITCH = HD * 2 + 32;   // LDS bytes per V row
+  static constexpr int CPR = HD / 8;           // 16-byte chunks per row
+  static constexpr int LOADS = kKeyTile * CPR / kPreThreads;  // chunks per thread per tensor per tile
+  static constexpr int LDS = kKeyTile * (KPITCH + VPITCH);
+};
+
+template <int HD, bool CHECK>
+__global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
+    const uint16_t* __restrict__ query, const int32_t* __restrict__ cu_q_lens,
+    const int32_t* __restrict__ chunk_offsets, const uint16_t* __restrict__ key_pool,
+    const uint16_t* __restrict__ value_pool, const int32_t* __restrict__ block_tables, int max_blocks, int q_tiles,
+    int num_q_heads, int num_kv_heads, int group, int num_blocks, int causal, float scale_log2,
+    void* __restrict__ out, int out_bf16, int32_t* err_flag) {
+  using C = PreCfg<HD>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  char* k_lds = smem;
+  char* v_lds = smem + kKeyTile * C::KPITCH;
+
+  // Work item: XCD-contiguous remap of the linear workgroup id.
+  const int items = gridDim.x, id = blockIdx.x;
+  const int w = (items % 8 == 0) ? (id % 8) * (items / 8) + id / 8 : id;
+  const int t = w % q_tiles;
+  int r = w / q_tiles;
+  const int hi = r % group;
+  r /= group;
+  const int g = r % num_kv_heads;
+  const int s = r / num_kv_heads;
+  const int h = g * group + hi;
+
+  const int qlo = cu_q_lens[s];
+  const int L = cu_q_lens[s + 1] - qlo;
+  const int off = chunk_offsets[s];
+  const int row0 = t * kPreTile;
+  if (row0 >= L) return;
+  if (off < 0 || static_cast<int64_t>(off) + L > static_cast<int64_t>(max_blocks) * kBlockSize) {
+    if (CHECK && threadIdx.x == 0 && t == 0 && hi == 0) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+    return;
+  }
+  const int kv_end = causal ? off + min(row0 + kPreTile, L) : off + L;
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int qc = lane & 31, hh = lane >> 5;
+  const int wrow0 = row0 + wave * kPreRows;
+  const int myrow = wrow0 + qc;
+  const bool row_ok = myrow < L;
+  const int qpos = off + myrow;
+  const int32_t* table = block_tables + static_cast<int64_t>(s) * max_blocks;
+
+  // Q^T as the B operand: lane (qc, hh) holds query row qc, head_dim 16ks + 8hh .. +7.
+  bf16x8 qf[C::KS];
+  {
+    const uint16_t* qrow = query + (static_cast<int64_t>(qlo + (row_ok ? myrow : 0)) * num_q_heads + h) * HD + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = row_ok ? as_bf16x8(ld16(qrow + 16 * ks)) : bf16x8{};
+  }
+
+  floatx16 acc[C::MD];
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[md][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  uint4 kreg[C::LOADS], vreg[C::LOADS];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int f = threadIdx.x + kPreThreads * i;
+      const int row = f / C::CPR, col = (f % C::CPR) * 8;
+      const int key = kt * kKeyTile + row;
+      uint4 kv = uint4{0, 0, 0, 0}, vv = uint4{0, 0, 0, 0};
+      if (key < kv_end) {
+        const int b = load_block_id<CHECK>(table, key / kBlockSize, num_blocks, err_flag);
+        if (b >= 0) {
+          const int64_t o = pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + col;
+          kv = ld16(key_pool + o);
+          vv = ld16(value_pool + o);
+        }
+      }
+      kreg[i] = kv;
+      vreg[i] = vv;
+    }
+  };
+
+  const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
+  load_tile(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();  // the previous tile's readers are done
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int f = threadIdx.x + kPreThreads * i;
+      const int row = f / C::CPR, col = (f % C::CPR) * 8;
+      st16(k_lds + row * C::KPITCH + col * 2, kreg[i]);
+      st16(v_lds + row * C::VPITCH + col * 2, vreg[i]);
+    }
+    __syncthreads();
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+
+    const int key0 = kt * kKeyTile;
+    const bool active = wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
+    if (active) {
+      floatx16 sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
+        const char* krow = k_lds + (32 * mt + qc) * C::KPITCH + 16 * hh;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+        }
+      }
+      // Element e = 4i + j of sacc[mt] is key key0 + 32mt + 8i + 4hh + j for query row qc.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const bool ok = key < kv_end && (!causal || key <= qpos);
+          const float v = ok ? sacc[mt][e] * scale_log2 : -INFINITY;
+          sacc[mt][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float psum = 0.f;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(sacc[mt][e] - m_use);
+          psum += p;
+          pb[2 * mt + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int md = 0; md < C::MD; ++md) acc[md] *= alpha;
+
+      // O^T += V^T P^T.  k-step a covers keys 16a + 4hh + e and 16a + 8 + 4hh + e (e = 0..3),
+      // matching pb[a]; the A operand lane (l % 32 = d, hh) reads those keys' V at d.
+      const int li = lane & 15, dg = (lane >> 4) & 1;
+      const uint16_t* vbase = reinterpret_cast<const uint16_t*>(v_lds);
+      constexpr int VP = C::VPITCH / 2;
+#pragma unroll
+      for (int md = 0; md < C::MD; ++md) {
+        const int col = 32 * md + 16 * dg + 4 * (li & 3);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int r0 = 16 * a + 4 * hh + (li >> 2);
+          const bf16x8 av = concat(lds_read_tr16(vbase + r0 * VP + col), lds_read_tr16(vbase + (r0 + 8) * VP + col));
+          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[a], acc[md], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
+#pragma unroll
+  for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * md + 8 * i + 4 * hh;
+      const float v0 = acc[md][4 * i] * inv, v1 = acc[md][4 * i + 1] * inv, v2 = acc[md][4 * i + 2] * inv,
+                  v3 = acc[md][4 * i + 3] * inv;
+      if (out_bf16) {
+        uint16_t* o = static_cast<uint16_t*>(out) + obase + d;
+        const uint2 pk = uint2{static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
+                               static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16)};
+        *reinterpret_cast<uint2*>(o) = pk;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + obase + d) = float4{v0, v1, v2, v3};
+      }
+    }
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* query,
+                                                   const int32_t* cu_q_lens, const int32_t* chunk_offsets,
+                                                   const void* key_pool, const void* value_pool,
+                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                   int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                                   int32_t causal, float scale, pkv_dtype dtype, int32_t* err_flag,
+                                                   void* stream) {
+  if (num_seqs < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || !std::isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !query || !cu_q_lens || !chunk_offsets || !key_pool || !value_pool || !block_tables)
+    return PKV_ERR_INVALID_ARG;
+  const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_q_heads * q_tiles;
+  if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  const float scale_log2 = scale * kLog2e;
+  const int ob = out_dtype == PKV_DTYPE_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+#define PKV_PRE(HD, CHECK)                                                                                      \
+  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK>), dim3(static_cast<unsigned>(items)), dim3(kPreThreads), 0, \
+                     st, static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets,                         \
+                     static_cast<const uint16_t*>(key_pool), static_cast<const uint16_t*>(value_pool),           \
+                     block_tables, max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks,    \
+                     causal != 0, scale_log2, out, ob, err_flag)
+#define PKV_PRE_HD(CHECK)                       \
+  switch (head_dim) {                           \
+    case 64: PKV_PRE(64, CHECK); break;         \
+    case 128: PKV_PRE(128, CHECK); break;       \
+    default: PKV_PRE(256, CHECK); break;        \
+  }
+  if (err_flag) { PKV_PRE_HD(true) } else { PKV_PRE_HD(false) }
+#undef PKV_PRE_HD
+#undef PKV_PRE
+  return pkv_host::launch_status();
+}

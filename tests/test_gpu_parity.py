@@ -1,0 +1,470 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Every call goes through the C ABI (via the ctypes binding).  Bars:
+  * slot mapping, cache write and paged gather: bit-exact (whole pools compared byte for byte);
+  * attention from bf16 inputs with fp32 accumulation: max-abs <= 1e-2 and mean-abs <= 1e-3
+    against the oracle on N(0,1) inputs;
+  * attention from fp32 inputs: max-abs <= 1e-4 (fp32 accumulation over at most a few thousand
+    terms plus the hardware exp2's ~1 ulp error stay far below this);
+  * physical-id permutation and repeated runs: bit-identical outputs; split size: within 5e-6.
+Parity runs in checked mode (err_flag given) with NaN-poisoned dead slots and out-of-range ids
+in unused block-table entries, so a stray read shows up as a NaN or a flag.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS, BF16_MEAN_ABS = 1e-2, 1e-3
+F32_MAX_ABS = 1e-4
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_170_amd as m
+    return m
+
+
+@pytest.fixture()
+def dev(pkv):
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(dev)
+
+
+def to_host_storage(t, dtype):
+    t = t.cpu()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def new_err(dev):
+    return torch.zeros(1, dtype=torch.int32, device=dev)
+
+
+def assert_close(got, ref, dtype, what):
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    diff = np.abs(got - ref)
+    if dtype == "f32":
+        assert diff.max() <= F32_MAX_ABS, f"{what}: max-abs {diff.max():.3e}"
+    else:
+        assert diff.max() <= BF16_MAX_ABS, f"{what}: max-abs {diff.max():.3e}"
+        assert diff.mean() <= BF16_MEAN_ABS, f"{what}: mean-abs {diff.mean():.3e}"
+    return float(diff.max()), float(diff.mean())
+
+
+class Dev:
+    """A case's pools and tables on the device."""
+
+    def __init__(self, case, dev):
+        self.c = case
+        self.dev = dev
+        self.kp = to_dev(case.key_pool, dev, case.dtype)
+        self.vp = to_dev(case.value_pool, dev, case.dtype)
+        self.bt = to_dev(case.block_tables, dev)
+        self.ctx = to_dev(case.context_lens, dev)
+
+
+def write_new_tokens(pkv, d: Dev, err, lo=None, hi=None, seqs=None):
+    """Slot-map and write the case's new tokens (optionally a sub-range of one sequence)."""
+    c = d.c
+    if lo is None:
+        cu, start, kn, vn = c.new_cu_lens, c.new_start_pos, c.key_new, c.value_new
+        bt = c.block_tables
+    else:
+        cu = np.array([0, hi - lo], np.int32)
+        start = np.array([lo], np.int32)
+        kn, vn = c.key_new[lo:hi], c.value_new[lo:hi]
+        bt = c.block_tables[seqs:seqs + 1]
+    T = int(cu[-1])
+    if T == 0:
+        return np.zeros(0, np.int32)
+    maxlen = int(np.diff(cu).max())
+    slots = pkv.slot_mapping(to_dev(bt, d.dev), to_dev(cu, d.dev), to_dev(start, d.dev), maxlen, c.num_blocks,
+                             err_flag=err, total=T)
+    pkv.cache_write(to_dev(kn, d.dev, c.dtype), to_dev(vn, d.dev, c.dtype), d.kp, d.vp, slots, err_flag=err)
+    ref_slots = oracle.slot_mapping(bt, cu, start, 16)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots), "slot mapping differs from the oracle"
+    return ref_slots
+
+
+def oracle_pools_after_write(c, slots):
+    return oracle.cache_write(c.key_pool, c.value_pool, c.key_new, c.value_new, slots)
+
+
+# ------------------------------------------------------------------------------------------
+# Integer / byte work: bit-exact
+# ------------------------------------------------------------------------------------------
+
+
+def test_tiny_write_and_gather_bit_exact(pkv, dev):
+    _say("case tiny_decode: slot mapping + cache write + paged gather (fp32, 295 tokens)")
+    c = wl.tiny_decode(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    assert to_host_storage(d.kp, c.dtype).tobytes() == rk.tobytes()
+    assert to_host_storage(d.vp, c.dtype).tobytes() == rv.tobytes()
+    cu = np.concatenate([[0], np.cumsum(c.context_lens)]).astype(np.int32)
+    kg, vg = pkv.paged_gather(d.kp, d.vp, d.bt, d.ctx, to_dev(cu, dev), int(c.context_lens.max()), int(cu[-1]),
+                              err_flag=err)
+    exp_k = np.concatenate([oracle.gather(rk, c.block_tables[s], int(c.context_lens[s])) for s in range(4)])
+    exp_v = np.concatenate([oracle.gather(rv, c.block_tables[s], int(c.context_lens[s])) for s in range(4)])
+    assert to_host_storage(kg, c.dtype).tobytes() == exp_k.tobytes()
+    assert to_host_storage(vg, c.dtype).tobytes() == exp_v.tobytes()
+    # Gathered rows are the generator's contiguous tokens again.
+    assert exp_k.tobytes() == c.key_new.tobytes()
+    assert int(err.item()) == 0
+
+
+def test_long_decode_write_bit_exact(pkv, dev):
+    _say("case long_decode: write of 58 x 16 tokens into the last blocks (bf16, 4x256)")
+    c = wl.long_decode(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    assert to_host_storage(d.kp, c.dtype).tobytes() == rk.tobytes()
+    assert to_host_storage(d.vp, c.dtype).tobytes() == rv.tobytes()
+    assert int(err.item()) == 0
+
+
+def test_write_skips_negative_slots_and_strided_rows(pkv, dev):
+    _say("case write: negative slots, strided key/value rows, fp32 and bf16")
+    for dtype in ("f32", "bf16"):
+        c = wl.random_case(3, kind="prefill", dtype=dtype, num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=64,
+                           max_ctx=200, q_len_max=40, poison=True)
+        d = Dev(c, dev)
+        err = new_err(dev)
+        slots = oracle.slot_mapping(c.block_tables, c.new_cu_lens, c.new_start_pos, 16)
+        slots[::3] = -1
+        # Rows taken from a wider buffer: token stride = 2 rows.
+        T = c.num_new_tokens
+        wide_k = np.zeros((T, 2, 4, 64), c.key_new.dtype)
+        wide_v = np.zeros((T, 2, 4, 64), c.key_new.dtype)
+        wide_k[:, 0] = c.key_new
+        wide_v[:, 0] = c.value_new
+        kt = to_dev(wide_k, dev, dtype)[:, 0]
+        vt = to_dev(wide_v, dev, dtype)[:, 0]
+        pkv.cache_write(kt, vt, d.kp, d.vp, to_dev(slots, dev), err_flag=err)
+        rk, rv = oracle.cache_write(c.key_pool, c.value_pool, c.key_new, c.value_new, slots)
+        assert to_host_storage(d.kp, dtype).tobytes() == rk.tobytes()
+        assert to_host_storage(d.vp, dtype).tobytes() == rv.tobytes()
+        assert int(err.item()) == 0
+
+
+def test_gather_bit_exact_gqa_decode(pkv, dev):
+    _say("case gqa_decode: paged gather of all 128 sequences (bf16, 8x128)")
+    c = wl.gqa_decode(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    cu = np.concatenate([[0], np.cumsum(c.context_lens)]).astype(np.int32)
+    kg, vg = pkv.paged_gather(d.kp, d.vp, d.bt, d.ctx, to_dev(cu, dev), int(c.context_lens.max()), int(cu[-1]),
+                              err_flag=err)
+    kh, vh = to_host_storage(kg, "bf16"), to_host_storage(vg, "bf16")
+    for s in range(c.num_seqs):
+        n = int(c.context_lens[s])
+        assert kh[cu[s]:cu[s] + n].tobytes() == oracle.gather(c.key_pool, c.block_tables[s], n).tobytes()
+        assert vh[cu[s]:cu[s] + n].tobytes() == oracle.gather(c.value_pool, c.block_tables[s], n).tobytes()
+    assert int(err.item()) == 0
+
+
+# ------------------------------------------------------------------------------------------
+# Decode
+# ------------------------------------------------------------------------------------------
+
+
+def _decode(pkv, d, **kw):
+    c = d.c
+    return pkv.paged_attn_decode(to_dev(c.query, d.dev, c.dtype), d.kp, d.vp, d.bt, d.ctx, c.scale, **kw)
+
+
+def test_tiny_decode_fp32(pkv, dev):
+    _say("case tiny_decode: write + decode, fp32, 8 heads x 64, contexts 17/50/100/128")
+    c = wl.tiny_decode(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, "f32")
+    for split in (0, 128):
+        out = _decode(pkv, d, err_flag=err, split_tokens=split)
+        assert_close(out.cpu().numpy(), ref, "f32", f"tiny decode split={split}")
+    assert int(err.item()) == 0
+
+
+def test_gqa_decode_full(pkv, dev):
+    _say("case gqa_decode: 128 seqs, 64/8 heads x 128, lognormal contexts, bf16 (whole output)")
+    c = wl.gqa_decode(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    out = _decode(pkv, d, err_flag=err)
+    ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
+    mx, mean = assert_close(out.cpu().numpy(), ref, "bf16", "gqa decode")
+    _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert int(err.item()) == 0
+
+
+def test_long_decode_full(pkv, dev):
+    _say("case long_decode: write 16 tokens/seq, then decode 58 x 4096, 16/4 heads x 256, bf16")
+    c = wl.long_decode(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    out = _decode(pkv, d, err_flag=err)
+    ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, "bf16")
+    mx, mean = assert_close(out.cpu().numpy(), ref, "bf16", "long decode")
+    _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert int(err.item()) == 0
+
+
+def test_decode_split_size_invariance_and_determinism(pkv, dev):
+    _say("case gqa_decode subset: split sizes 128..1024, repeated runs")
+    c = wl.random_case(91, kind="decode", dtype="bf16", num_seqs=9, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                       max_ctx=2100, min_ctx=1, new_tokens=False, poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    outs = {s: _decode(pkv, d, err_flag=err, split_tokens=s).cpu().numpy() for s in (128, 256, 512, 1024)}
+    base = outs[512]
+    for s, o in outs.items():
+        assert np.max(np.abs(o - base)) <= 5e-6, f"split {s}"
+    again = _decode(pkv, d, err_flag=err, split_tokens=512).cpu().numpy()
+    assert again.tobytes() == base.tobytes()
+    ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
+    assert_close(base, ref, "bf16", "split decode")
+    assert int(err.item()) == 0
+
+
+def test_decode_block_permutation_bit_identical(pkv, dev):
+    _say("case decode permutation: same data under permuted physical block ids")
+    c = wl.random_case(92, kind="decode", dtype="bf16", num_seqs=6, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                       max_ctx=700, min_ctx=1, new_tokens=False, poison=True)
+    rng = np.random.default_rng(9)
+    perm = rng.permutation(c.num_blocks).astype(np.int32)
+    kp = np.empty_like(c.key_pool)
+    vp = np.empty_like(c.value_pool)
+    kp[perm] = c.key_pool
+    vp[perm] = c.value_pool
+    bt = c.block_tables.copy()
+    used = bt != wl.UNUSED_BLOCK_ID
+    bt[used] = perm[bt[used]]
+    d1 = Dev(c, dev)
+    err = new_err(dev)
+    o1 = _decode(pkv, d1, err_flag=err, split_tokens=256).cpu().numpy()
+    c2 = wl.PagedCase(**{**c.__dict__, "key_pool": kp, "value_pool": vp, "block_tables": bt})
+    d2 = Dev(c2, dev)
+    o2 = _decode(pkv, d2, err_flag=err, split_tokens=256).cpu().numpy()
+    assert o1.tobytes() == o2.tobytes()
+    assert int(err.item()) == 0
+
+
+DECODE_SWEEP = [
+    # (dtype, hq, hkv, hd, max_ctx, min_ctx)
+    ("bf16", 8, 8, 64, 300, 0),
+    ("bf16", 16, 8, 128, 200, 1),
+    ("bf16", 16, 4, 128, 600, 1),
+    ("bf16", 16, 1, 128, 1300, 1),
+    ("bf16", 4, 1, 256, 900, 1),
+    ("bf16", 32, 2, 64, 100, 1),
+    ("f32", 8, 2, 64, 400, 0),
+    ("f32", 16, 1, 128, 300, 1),
+    ("f32", 4, 4, 256, 200, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,hd,max_ctx,min_ctx", DECODE_SWEEP)
+def test_decode_sweep(pkv, dev, dtype, hq, hkv, hd, max_ctx, min_ctx):
+    _say(f"case decode sweep: {dtype} hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx}")
+    c = wl.random_case(hq * 7 + hd + max_ctx, kind="decode", dtype=dtype, num_seqs=7, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, min_ctx=min_ctx, poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, dtype)
+    for split in (0, 128):
+        out = _decode(pkv, d, err_flag=err, split_tokens=split)
+        assert_close(out.cpu().numpy(), ref, dtype, f"decode sweep split={split}")
+    assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("ctx_list", [[0, 1, 15, 16, 17], [31, 32, 33, 127, 128], [129, 511, 512, 513, 1]])
+def test_decode_edge_contexts(pkv, dev, ctx_list):
+    _say(f"case decode edges: contexts {ctx_list}")
+    c = wl.random_case(77, kind="decode", dtype="bf16", num_seqs=len(ctx_list), num_q_heads=8, num_kv_heads=2,
+                       head_dim=128, max_ctx=600, min_ctx=0, poison=True, new_tokens=False)
+    # Rebuild tables for the exact contexts.
+    ctx = np.array(ctx_list, np.int32)
+    need = [math.ceil(x / 16) for x in ctx]
+    nblk = sum(need) + 2
+    free = np.random.default_rng(5).permutation(nblk).astype(np.int32)
+    bt = wl.allocate_from_free_list(free, need, max(need) + 1)
+    shape = (nblk, 16, 2, 128)
+    rng = np.random.default_rng(6)
+    kp = wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    vp = wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    live = wl.live_slot_mask(bt, ctx, nblk)
+    kp[~live] = wl.BF16_NAN_BITS
+    vp[~live] = wl.BF16_NAN_BITS
+    c2 = wl.PagedCase(**{**c.__dict__, "key_pool": kp, "value_pool": vp, "block_tables": bt, "context_lens": ctx,
+                         "num_blocks": nblk})
+    d = Dev(c2, dev)
+    err = new_err(dev)
+    ref = oracle.decode(c2.query, kp, vp, bt, ctx, c2.scale, "bf16")
+    for split in (0, 128, 256):
+        out = _decode(pkv, d, err_flag=err, split_tokens=split).cpu().numpy()
+        assert_close(out, ref, "bf16", f"edge decode split={split}")
+        assert (out[ctx == 0] == 0).all()
+    assert int(err.item()) == 0
+
+
+def test_decode_bf16_output(pkv, dev):
+    _say("case decode bf16 output")
+    c = wl.random_case(93, kind="decode", dtype="bf16", num_seqs=5, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                       max_ctx=1500, min_ctx=1, new_tokens=False, poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    out = _decode(pkv, d, err_flag=err, out_dtype=torch.bfloat16).float().cpu().numpy()
+    ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
+    diff = np.abs(out - ref)
+    # bf16 rounding of the result adds at most half an ulp (2^-9 relative).
+    assert (diff <= BF16_MAX_ABS + np.abs(ref) * 2.0 ** -8).all()
+    assert diff.mean() <= BF16_MEAN_ABS + np.mean(np.abs(ref)) * 2.0 ** -9
+    assert int(err.item()) == 0
+
+
+# ------------------------------------------------------------------------------------------
+# Prefill chunk
+# ------------------------------------------------------------------------------------------
+
+
+def _prefill(pkv, d, q, cu, offs, max_q_len, causal=True, **kw):
+    c = d.c
+    return pkv.paged_attn_prefill_chunk(to_dev(q, d.dev, c.dtype), to_dev(cu, d.dev), to_dev(offs, d.dev), d.kp,
+                                        d.vp, d.bt, max_q_len, c.scale, causal=causal, **kw)
+
+
+def test_chunked_prefill_equals_one_pass(pkv, dev):
+    _say("case chunked_prefill: 1000 tokens in chunks 256/256/256/232 vs one pass, 8 heads x 64, bf16")
+    c = wl.chunked_prefill(poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    outs = []
+    kp_ref, vp_ref = c.key_pool, c.value_pool
+    for (s, e) in c.notes["chunks"]:
+        write_new_tokens(pkv, d, err, lo=s, hi=e, seqs=0)
+        rs = oracle.slot_mapping(c.block_tables, np.array([0, e - s], np.int32), np.array([s], np.int32), 16)
+        kp_ref, vp_ref = oracle.cache_write(kp_ref, vp_ref, c.key_new[s:e], c.value_new[s:e], rs)
+        cu = np.array([0, e - s], np.int32)
+        offs = np.array([s], np.int32)
+        out = _prefill(pkv, d, c.query[s:e], cu, offs, e - s, err_flag=err).cpu().numpy()
+        ref = oracle.prefill_chunk(c.query[s:e], cu, offs, kp_ref, vp_ref, c.block_tables, c.scale, "bf16")
+        assert_close(out, ref, "bf16", f"chunk {s}:{e}")
+        outs.append(out)
+    assert to_host_storage(d.kp, "bf16").tobytes() == kp_ref.tobytes()
+    one = oracle.prefill_chunk(c.query, np.array([0, 1000], np.int32), np.array([0], np.int32), kp_ref, vp_ref,
+                               c.block_tables, c.scale, "bf16")
+    mx, mean = assert_close(np.concatenate(outs), one, "bf16", "chunked vs one pass")
+    _say(f"  chunked GPU vs one-pass oracle: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    # The GPU's own one-pass result over the whole prompt agrees with its chunked result.
+    gpu_one = _prefill(pkv, d, c.query, np.array([0, 1000], np.int32), np.array([0], np.int32), 1000,
+                       err_flag=err).cpu().numpy()
+    assert_close(gpu_one, one, "bf16", "one pass")
+    assert np.max(np.abs(gpu_one - np.concatenate(outs))) <= 2 * BF16_MAX_ABS
+    assert int(err.item()) == 0
+
+
+PREFILL_SWEEP = [
+    # (hq, hkv, hd, max_ctx, q_len_max, causal)
+    (8, 8, 64, 400, 150, True),
+    (16, 2, 128, 700, 300, True),
+    (8, 1, 128, 300, 129, False),
+    (4, 4, 256, 500, 200, True),
+    (16, 16, 64, 260, 1, True),
+    (32, 2, 128, 1200, 513, True),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,hd,max_ctx,q_len_max,causal", PREFILL_SWEEP)
+def test_prefill_sweep(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, causal):
+    _say(f"case prefill sweep: hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx} L<={q_len_max} causal={causal}")
+    c = wl.random_case(hq + 3 * hd + max_ctx + q_len_max, kind="prefill", dtype="bf16", num_seqs=5, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, q_len_max=q_len_max, causal=causal,
+                       poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    maxl = int(np.diff(c.cu_q_lens).max())
+    out = _prefill(pkv, d, c.query, c.cu_q_lens, c.chunk_offsets, maxl, causal=causal, err_flag=err).cpu().numpy()
+    ref = oracle.prefill_chunk(c.query, c.cu_q_lens, c.chunk_offsets, rk, rv, c.block_tables, c.scale, "bf16",
+                               causal=causal)
+    assert_close(out, ref, "bf16", "prefill sweep")
+    assert int(err.item()) == 0
+
+
+def test_mixed_step(pkv, dev):
+    _say("case mixed_step: write 512 -> decode 127 seqs (shared 63-block prefix) -> prefill 512 @ 16384")
+    dec, pre = wl.mixed_step(poison=True)
+    d = Dev(pre, dev)  # pools shared by both parts
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(pre, slots)
+    dd = Dev.__new__(Dev)
+    dd.c, dd.dev, dd.kp, dd.vp = dec, dev, d.kp, d.vp
+    dd.bt, dd.ctx = to_dev(dec.block_tables, dev), to_dev(dec.context_lens, dev)
+    out_dec = _decode(pkv, dd, err_flag=err).cpu().numpy()
+    out_pre = _prefill(pkv, d, pre.query, pre.cu_q_lens, pre.chunk_offsets, 512, err_flag=err).cpu().numpy()
+    assert int(err.item()) == 0
+    ref_dec = oracle.decode(dec.query, rk, rv, dec.block_tables, dec.context_lens, dec.scale, "bf16")
+    mx, mean = assert_close(out_dec, ref_dec, "bf16", "mixed decode")
+    _say(f"  decode max-abs {mx:.2e} mean-abs {mean:.2e}")
+    rows = np.unique(np.concatenate([np.arange(0, 512, 5), np.arange(496, 512)]))
+    ref_pre = oracle.prefill_chunk(pre.query, pre.cu_q_lens, pre.chunk_offsets, rk, rv, pre.block_tables, pre.scale,
+                                   "bf16", rows=rows)
+    mx, mean = assert_close(out_pre[rows], ref_pre[rows], "bf16", "mixed prefill (sampled rows)")
+    _say(f"  prefill ({len(rows)} sampled rows) max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert np.isfinite(out_pre).all()
+
+
+def test_prefill_bf16_output_and_determinism(pkv, dev):
+    _say("case prefill bf16 output + repeat")
+    c = wl.random_case(94, kind="prefill", dtype="bf16", num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                       max_ctx=600, q_len_max=260, poison=True)
+    d = Dev(c, dev)
+    err = new_err(dev)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    maxl = int(np.diff(c.cu_q_lens).max())
+    o32a = _prefill(pkv, d, c.query, c.cu_q_lens, c.chunk_offsets, maxl, err_flag=err).cpu().numpy()
+    o32b = _prefill(pkv, d, c.query, c.cu_q_lens, c.chunk_offsets, maxl, err_flag=err).cpu().numpy()
+    assert o32a.tobytes() == o32b.tobytes()
+    ob = _prefill(pkv, d, c.query, c.cu_q_lens, c.chunk_offsets, maxl, err_flag=err,
+                  out_dtype=torch.bfloat16).float().cpu().numpy()
+    ref = oracle.prefill_chunk(c.query, c.cu_q_lens, c.chunk_offsets, rk, rv, c.block_tables, c.scale, "bf16")
+    diff = np.abs(ob - ref)
+    assert (diff <= BF16_MAX_ABS + np.abs(ref) * 2.0 ** -8).all()
+    assert int(err.item()) == 0
