@@ -1,0 +1,283 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+A step is one pass of the whole path over the mixed chunked-prefill + decode workload
+(70B-style GQA layer: 64 query heads / 8 KV heads x 128, bf16, 16-token blocks):
+  1. slot mapping of the 512 new prompt tokens (chunk at offset 16,384 of a 32,768-token prompt),
+  2. cache write of their K/V into the pool,
+  3. decode of 127 sequences (contexts uniform in 200..8192, a shared 63-block prefix),
+  4. prefill-chunk attention of the 512 rows over 16,384 cached + 512 causal positions,
+all enqueued on one stream with inputs resident in HBM.
+
+Printed: one JSON line.  `value` is the decode KV-read bandwidth in GB/s over unique pool bytes
+(the shared prefix counted once); the prefill chunk's TFLOP/s and both fractions of peak are in
+`secondary`; `roofline` describes the kernel that takes the most time per step.  Per-kernel
+times come from HIP events on the launch stream.  `cpu_baseline` times the fp64 oracle on this
+host on the same inputs (decode of every sequence, prefill of a sample of rows).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # dense: 256 CUs x 2.4 GHz x 4096 flop/clk
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed_step", choices=["mixed_step", "gqa_decode", "long_decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=64, help="prefill rows timed in the oracle baseline")
+    return ap.parse_args()
+
+
+def sources_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_170_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "paged_kv_cache_170_amd", "csrc", "common.hpp"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_key: str, src: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken on these sources."""
+    path = os.path.join(PROFILES, f"counters_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_hash") != sources_hash([src]):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def unique_kv_bytes(case) -> int:
+    """K+V bytes of the distinct pool rows the decode reads (shared blocks counted once)."""
+    rows = set()
+    for s in range(case.num_seqs):
+        n = int(case.context_lens[s])
+        nb = -(-n // 16)
+        for j in range(nb):
+            b = int(case.block_tables[s, j])
+            cnt = 16 if j < nb - 1 else n - 16 * (nb - 1)
+            rows.update(b * 16 + o for o in range(cnt))
+    return len(rows) * 2 * case.num_kv_heads * case.head_dim * case.elem_bytes
+
+
+def decode_algorithmic_bytes(case, out_bytes=4):
+    kv = unique_kv_bytes(case)
+    logical = int(case.context_lens.astype(np.int64).sum()) * 2 * case.num_kv_heads * case.head_dim * case.elem_bytes
+    q = case.num_seqs * case.num_q_heads * case.head_dim * case.elem_bytes
+    o = case.num_seqs * case.num_q_heads * case.head_dim * out_bytes
+    table = 4 * int(sum(-(-int(n) // 16) for n in case.context_lens))
+    return kv + q + o + table + 4 * case.num_seqs, kv, logical
+
+
+def prefill_flops(case) -> int:
+    total = 0
+    for s in range(len(case.chunk_offsets)):
+        L = int(case.cu_q_lens[s + 1] - case.cu_q_lens[s])
+        o = int(case.chunk_offsets[s])
+        vis = L * o + L * (L + 1) // 2 if case.causal else L * (o + L)
+        total += vis
+    return 4 * case.head_dim * case.num_q_heads * total
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the kernels run on a "
+              f"single device; sharding is described in the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_170_amd as pkv
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    if args.workload == "mixed_step":
+        dec, pre = wl.mixed_step(poison=False)
+    elif args.workload == "gqa_decode":
+        dec, pre = wl.gqa_decode(poison=False), None
+    else:
+        dec, pre = wl.long_decode(poison=False), None
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] workload {args.workload} generated in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    def to_dev(a, bf16=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+    bf = dec.dtype == "bf16"
+    kp, vp = to_dev(dec.key_pool, bf), to_dev(dec.value_pool, bf)
+    # The new tokens of this step (the prefill chunk for the mixed step, the last block per
+    # sequence for long decode).
+    wcase = pre if pre is not None else dec
+    has_write = wcase.num_new_tokens > 0
+    if has_write:
+        w_bt = to_dev(wcase.block_tables)
+        w_cu = to_dev(wcase.new_cu_lens)
+        w_start = to_dev(wcase.new_start_pos)
+        w_k, w_v = to_dev(wcase.key_new, bf), to_dev(wcase.value_new, bf)
+        w_max = int(np.diff(wcase.new_cu_lens).max())
+        slots = torch.empty(wcase.num_new_tokens, dtype=torch.int32, device=dev)
+    d_q = to_dev(dec.query, bf)
+    d_bt, d_ctx = to_dev(dec.block_tables), to_dev(dec.context_lens)
+    d_out = torch.empty((dec.num_seqs, dec.num_q_heads, dec.head_dim), dtype=torch.float32, device=dev)
+    ws = pkv.decode_workspace(d_q, dec.num_kv_heads, dec.max_blocks_per_seq)
+    if pre is not None:
+        p_q = to_dev(pre.query, bf)
+        p_cu, p_off, p_bt = to_dev(pre.cu_q_lens), to_dev(pre.chunk_offsets), to_dev(pre.block_tables)
+        p_out = torch.empty((pre.query.shape[0], pre.num_q_heads, pre.head_dim), dtype=torch.float32, device=dev)
+        p_maxl = int(np.diff(pre.cu_q_lens).max())
+    torch.cuda.synchronize()
+
+    names = ["slot_mapping", "cache_write", "decode", "prefill"]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        if has_write:
+            pkv.slot_mapping(w_bt, w_cu, w_start, w_max, dec.num_blocks, out=slots)
+        mark(1)
+        if has_write:
+            pkv.cache_write(w_k, w_v, kp, vp, slots)
+        mark(2)
+        pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=d_out, workspace=ws)
+        mark(3)
+        if pre is not None:
+            pkv.paged_attn_prefill_chunk(p_q, p_cu, p_off, kp, vp, p_bt, p_maxl, pre.scale, causal=True, out=p_out)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            per[n].append(ev[i].elapsed_time(ev[i + 1]))
+    avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
+    med_ms = {n: float(np.median(v)) for n, v in per.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps in {wall:.3f}s; per-kernel avg ms "
+          + ", ".join(f"{n}={avg_ms[n]:.4f}" for n in names), file=sys.stderr, flush=True)
+
+    dec_bytes, dec_kv_unique, dec_kv_logical = decode_algorithmic_bytes(dec)
+    dec_s = avg_ms["decode"] * 1e-3
+    dec_gbs = dec_bytes / dec_s / 1e9
+    secondary = {
+        "decode_ms": avg_ms["decode"],
+        "decode_gbs_unique": dec_gbs,
+        "decode_frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
+        "decode_gbs_logical": (dec_bytes - dec_kv_unique + dec_kv_logical) / dec_s / 1e9,
+        "decode_kv_bytes_unique": dec_kv_unique,
+        "decode_kv_bytes_logical": dec_kv_logical,
+    }
+    kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs, HBM_PEAK_GBS, "GB/s", "decode.hip")}
+    if pre is not None:
+        fl = prefill_flops(pre)
+        pre_tf = fl / (avg_ms["prefill"] * 1e-3) / 1e12
+        secondary.update({"prefill_ms": avg_ms["prefill"], "prefill_flop": fl, "prefill_tflops": pre_tf,
+                          "prefill_frac_mfma_peak": pre_tf / BF16_MFMA_PEAK_TFLOPS})
+        kernels["prefill"] = (avg_ms["prefill"], "mfma", fl, pre_tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s", "prefill.hip")
+    if has_write:
+        wb = 2 * wcase.num_new_tokens * wcase.num_kv_heads * wcase.head_dim * wcase.elem_bytes * 2 + 4 * wcase.num_new_tokens
+        secondary.update({"cache_write_ms": avg_ms["cache_write"], "slot_mapping_ms": avg_ms["slot_mapping"],
+                          "cache_write_gbs": wb / (avg_ms["cache_write"] * 1e-3) / 1e9})
+    dominant = max(kernels, key=lambda k: kernels[k][0])
+    ms, bound, work, achieved, peak, unit, src = kernels[dominant]
+    roofline = {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": counter_traffic(f"{dominant}_{args.workload}", src),
+                "work_per_launch": work, "avg_launch_ms": ms}
+    for k, (ms_k, bound_k, work_k, ach_k, peak_k, unit_k, src_k) in kernels.items():
+        secondary[f"roofline_{k}"] = {"bound": bound_k, "achieved": ach_k, "peak": peak_k, "unit": unit_k,
+                                      "frac": ach_k / peak_k,
+                                      "traffic": counter_traffic(f"{k}_{args.workload}", src_k)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dec, pre, kp, vp, has_write, args, torch)
+
+    config = {"workload": args.workload, "num_seqs_decode": dec.num_seqs, "q_heads": dec.num_q_heads,
+              "kv_heads": dec.num_kv_heads, "head_dim": dec.head_dim, "block_size": 16,
+              "context_lens": "uniform 200..8192, shared 63-block prefix" if args.workload == "mixed_step" else
+              ("lognormal mean 1500, sd 600, clipped 16..8192" if args.workload == "gqa_decode" else "4096 each"),
+              "seed": {"mixed_step": 5, "gqa_decode": 3, "long_decode": 4}[args.workload]}
+    if pre is not None:
+        config.update({"prefill_chunk": int(pre.cu_q_lens[-1]), "prefill_offset": int(pre.chunk_offsets[0])})
+    line = {"metric": "paged decode KV-read GB/s (% HBM peak); chunked-prefill TFLOP/s (% MFMA)",
+            "value": dec_gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if bf else "f32", "data": "synthetic", "config": config,
+            "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+            "kernel_ms_median": med_ms}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(dec, pre, kp, vp, has_write, args, torch):
+    """The fp64 oracle on this host: decode of every sequence, prefill of a row sample."""
+    import oracle
+
+    kpool = kp.cpu().view(torch.int16).numpy().view(np.uint16) if dec.dtype == "bf16" else kp.cpu().numpy()
+    vpool = vp.cpu().view(torch.int16).numpy().view(np.uint16) if dec.dtype == "bf16" else vp.cpu().numpy()
+    t = time.perf_counter()
+    oracle.decode(dec.query, kpool, vpool, dec.block_tables, dec.context_lens, dec.scale, dec.dtype)
+    dt_dec = time.perf_counter() - t
+    dec_bytes, _, _ = decode_algorithmic_bytes(dec)
+    res = {"value": dec_bytes / dt_dec / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+           "sample": f"decode of all {dec.num_seqs} sequences ({dt_dec:.1f}s)",
+           "host_cpus": len(os.sched_getaffinity(0))}
+    if pre is not None:
+        rows = np.linspace(0, int(pre.cu_q_lens[-1]) - 1, args.cpu_sample_rows).astype(int)
+        t = time.perf_counter()
+        oracle.prefill_chunk(pre.query, pre.cu_q_lens, pre.chunk_offsets, kpool, vpool, pre.block_tables, pre.scale,
+                             pre.dtype, rows=rows)
+        dt_pre = time.perf_counter() - t
+        o = int(pre.chunk_offsets[0])
+        fl = 4 * pre.head_dim * pre.num_q_heads * int(sum(o + r + 1 for r in rows))
+        res["prefill_gflops"] = fl / dt_pre / 1e9
+        res["sample"] += f"; prefill of {len(rows)} of {int(pre.cu_q_lens[-1])} rows ({dt_pre:.1f}s)"
+    return res
+
+
+if __name__ == "__main__":
+    main()

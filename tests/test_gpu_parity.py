@@ -248,13 +248,16 @@ def test_decode_split_size_invariance_and_determinism(pkv, dev):
     d = Dev(c, dev)
     err = new_err(dev)
     outs = {s: _decode(pkv, d, err_flag=err, split_tokens=s).cpu().numpy() for s in (128, 256, 512, 1024)}
+    ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
     base = outs[512]
     for s, o in outs.items():
-        assert np.max(np.abs(o - base)) <= 5e-6, f"split {s}"
+        assert_close(o, ref, "bf16", f"split {s}")
+        # Each split rescales and rounds its probabilities to bf16 for the P.V product on its own
+        # running max, so split sizes agree to the bf16 rounding of P (2^-9 relative per weight),
+        # not to fp32 rounding.
+        assert np.max(np.abs(o - base)) <= 5e-3, f"split {s} vs 512"
     again = _decode(pkv, d, err_flag=err, split_tokens=512).cpu().numpy()
     assert again.tobytes() == base.tobytes()
-    ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
-    assert_close(base, ref, "bf16", "split decode")
     assert int(err.item()) == 0
 
 
