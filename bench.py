@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--workload", default="mixed_step", choices=["mixed_step", "gqa_decode", "long_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=64, help="prefill rows timed in the oracle baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run a plain fp32 copy kernel over this many MiB (a known-size reference "
+                         "for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -161,6 +164,17 @@ def main():
         p_maxl = int(np.diff(pre.cu_q_lens).max())
     torch.cuda.synchronize()
 
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] copy reference: 3 x ({args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written)",
+              file=sys.stderr, flush=True)
+
     names = ["slot_mapping", "cache_write", "decode", "prefill"]
     stream = torch.cuda.current_stream(dev)
 
@@ -201,6 +215,18 @@ def main():
     print(f"[bench] {args.steps} steps in {wall:.3f}s; per-kernel avg ms "
           + ", ".join(f"{n}={avg_ms[n]:.4f}" for n in names), file=sys.stderr, flush=True)
 
+    # Bandwidth a plain read stream reaches on this device: read the whole key pool (>= 1 GB).
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pkv.stream_read_probe(kp, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        pkv.stream_read_probe(kp, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stream_gbs = 5 * kp.numel() * kp.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
     dec_bytes, dec_kv_unique, dec_kv_logical = decode_algorithmic_bytes(dec)
     dec_s = avg_ms["decode"] * 1e-3
     dec_gbs = dec_bytes / dec_s / 1e9
@@ -211,6 +237,8 @@ def main():
         "decode_gbs_logical": (dec_bytes - dec_kv_unique + dec_kv_logical) / dec_s / 1e9,
         "decode_kv_bytes_unique": dec_kv_unique,
         "decode_kv_bytes_logical": dec_kv_logical,
+        "stream_read_gbs": stream_gbs,
+        "decode_frac_of_stream_read": dec_gbs / stream_gbs,
     }
     kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs, HBM_PEAK_GBS, "GB/s", "decode.hip")}
     if pre is not None:

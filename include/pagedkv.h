@@ -148,7 +148,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   out                 [num_seqs, num_q_heads, head_dim], dtype out_dtype
  *   query               [num_seqs, num_q_heads, head_dim], dtype `dtype` (the pool dtype)
  *   context_lens        int32 [num_seqs] (device), each <= max_blocks_per_seq * 16
- *   split_tokens        0 for the default, else a positive multiple of 128
+ *   scale               > 0 (the usual 1/sqrt(head_dim)); other values are PKV_ERR_INVALID_ARG
+ *   split_tokens        0 for the default, else a multiple of 128 in [128, 1024]
  *   workspace           device scratch of >= pkv_decode_workspace_bytes(...) bytes; contents on
  *                       entry are ignored; must not be shared by calls running concurrently.
  */
@@ -170,6 +171,7 @@ pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* que
  *   cu_q_lens           int32 [num_seqs + 1] (device), non-decreasing from 0
  *   chunk_offsets       int32 [num_seqs] (device), >= 0
  *   max_q_len           host upper bound of L_s (sizes the grid; rows beyond it are not computed)
+ *   scale               > 0 (the usual 1/sqrt(head_dim)); other values are PKV_ERR_INVALID_ARG
  */
 pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* query, const int32_t* cu_q_lens,
                                         const int32_t* chunk_offsets, const void* key_pool, const void* value_pool,
@@ -177,6 +179,14 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
                                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t num_blocks, int32_t causal, float scale,
                                         pkv_dtype dtype, int32_t* err_flag, void* stream);
+
+/*
+ * Streaming-read reference (not part of the attention path): reads `bytes` bytes at `buf` (device,
+ * 16-byte aligned, bytes % 16 == 0) once with 16-byte loads and XORs a fold of them into *sink
+ * (a device uint32).  Its duration gives the bandwidth a plain read stream reaches on the device,
+ * against which the decode's bandwidth is compared.
+ */
+pkv_status pkv_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

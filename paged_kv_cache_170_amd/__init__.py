@@ -44,6 +44,7 @@ _SIGS = {
                                      _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
+    "pkv_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -230,3 +231,10 @@ def paged_attn_prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk
                                              _ptr(err_flag), _stream(query.device)),
            "pkv_paged_attn_prefill_chunk")
     return out
+
+
+def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read every byte of `buf` once (bandwidth reference); folds into the uint32-sized `sink`."""
+    _need_gpu(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.pkv_stream_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)), "pkv_stream_read_probe")

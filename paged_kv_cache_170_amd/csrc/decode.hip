@@ -7,8 +7,10 @@
 // online softmax; here the walk is split over workgroups and the partial states are merged.
 //
 // Design (gfx950, wave64):
-//   * grid (split, kv_head, seq); a workgroup of 4 waves owns `split_tokens` positions of one
-//     (sequence, KV head) and serves all G query heads of that group from each loaded page.
+//   * a persistent grid walks the compact list of (sequence, split, KV head) items (built on the
+//     device from context_lens, so no workgroup is launched idle); a workgroup of 4 waves owns
+//     `split_tokens` positions of one (sequence, KV head) and serves all G query heads of that
+//     group from each loaded page.
 //   * a wave step covers 32 positions = two 16-token blocks.  K is loaded straight into MFMA
 //     operand registers; S^T = K Q^T uses v_mfma_f32_16x16x32_bf16 with the 16 MFMA columns
 //     holding the G query heads (zero-padded).  V rows are staged in LDS in their natural layout
@@ -27,6 +29,7 @@ namespace pkv {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kMaxGroup = 16;
+constexpr float kRescaleGap = 8.f;  // log2 units the running max may trail a step's max
 
 template <int HD>
 struct DecCfg {
@@ -92,30 +95,51 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int32_t* err_f
   return ctx;
 }
 
-template <int HD, bool CHECK>
-__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
-    const uint16_t* __restrict__ query, const uint16_t* __restrict__ key_pool, const uint16_t* __restrict__ value_pool,
-    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ context_lens,
-    int num_q_heads, int num_kv_heads, int group, int num_blocks, float scale_log2, int split_tokens, int max_splits,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ out, int out_bf16, int32_t* err_flag) {
-  using C = DecCfg<HD>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int ctx = clamp_ctx<CHECK>(context_lens[s], max_blocks, err_flag, split == 0 && g == 0 && threadIdx.x == 0);
-  const int nsplit = (ctx + split_tokens - 1) / split_tokens;
-  if (ctx == 0) {
-    if (split != 0) return;
-    for (int i = threadIdx.x; i < group * HD; i += kDecThreads)
-      store_out(out, (static_cast<int64_t>(s) * num_q_heads + g * group) * HD + i, 0.f, out_bf16);
-    return;
-  }
-  if (split >= nsplit) return;
+// Kernel arguments of the bf16 decode (one struct so that every launch form shares them).
+struct DecArgs {
+  const uint16_t* query;
+  const uint16_t* key_pool;
+  const uint16_t* value_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_o;
+  float* ws_ml;
+  void* out;
+  int32_t* err_flag;
+  int max_blocks, num_q_heads, num_kv_heads, group, num_blocks, split_tokens, max_splits, out_bf16;
+  float scale_log2;
+};
 
+template <int HD>
+struct DecBuf {
+  uint4 k[2][DecCfg<HD>::KK];
+  uint4 v[2][DecCfg<HD>::VLD];
+  int b0, b1;
+};
+
+// One work item: positions [split * split_tokens, min(+split_tokens, ctx)) of sequence s, KV head g,
+// for all query heads of the group.  Called by all 256 threads of the workgroup.
+template <int HD, bool CHECK, bool PREFETCH>
+__device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g, int split, int ctx, int nsplit,
+                                                 char* smem) {
+  using C = DecCfg<HD>;
+  const uint16_t* __restrict__ query = A_.query;
+  const uint16_t* __restrict__ key_pool = A_.key_pool;
+  const uint16_t* __restrict__ value_pool = A_.value_pool;
+  const int num_q_heads = A_.num_q_heads, num_kv_heads = A_.num_kv_heads, group = A_.group;
+  const int num_blocks = A_.num_blocks, split_tokens = A_.split_tokens;
+  const float scale_log2 = A_.scale_log2;
+  int32_t* err_flag = A_.err_flag;
+  constexpr bool kPrefetch = PREFETCH;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, c = lane >> 4;
   const int tok0 = split * split_tokens;
   const int tok_end = min(tok0 + split_tokens, ctx);
-  const int32_t* table = block_tables + static_cast<int64_t>(s) * max_blocks;
+  const int32_t* table = A_.block_tables + static_cast<int64_t>(s) * A_.max_blocks;
+
+  // The split's block ids, one per lane (a split spans at most 64 blocks).
+  const int nblk_split = (tok_end - tok0 + kBlockSize - 1) / kBlockSize;
+  const int my_id = lane < nblk_split ? load_block_id<CHECK>(table, tok0 / kBlockSize + lane, num_blocks, err_flag) : -1;
 
   // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.
   bf16x8 qf[C::KK];
@@ -126,7 +150,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
     for (int kk = 0; kk < C::KK; ++kk) qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
   floatx4 acc[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -134,36 +158,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
   uint16_t* vstage = reinterpret_cast<uint16_t*>(smem + wave * C::STAGE);
   constexpr int VP = C::VPITCH / 2;  // pitch in elements
   const int units = (tok_end - tok0 + 31) / 32;
+  const int vrow_base = lane / C::LPR, vcol = (lane % C::LPR) * 8;
 
-  for (int u = wave; u < units; u += kDecWaves) {
+  // Step u covers positions tok0 + 32u .. +31 (two blocks).  Issue all of its loads.
+  auto load = [&](int u, DecBuf<HD>& B) {
     const int t0 = tok0 + 32 * u;
-    const int j0 = t0 / kBlockSize;
-    const bool has1 = t0 + kBlockSize < ctx;
-    const int b0 = load_block_id<CHECK>(table, j0, num_blocks, err_flag);
-    const int b1 = has1 ? load_block_id<CHECK>(table, j0 + 1, num_blocks, err_flag) : -1;
-
-    // Issue every load of the step before any use.
-    uint4 kf[2][C::KK];
-    uint4 vf[2][C::VLD];
-    const int vrow_base = lane / C::LPR, vcol = (lane % C::LPR) * 8;
+    B.b0 = __builtin_amdgcn_readlane(my_id, 2 * u);
+    B.b1 = (t0 + kBlockSize < ctx) ? __builtin_amdgcn_readlane(my_id, 2 * u + 1) : -1;
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
-      const int b = pg ? b1 : b0;
+      const int b = pg ? B.b1 : B.b0;
       if (b >= 0) {
         const uint16_t* kb = key_pool + pool_row_offset(b, n, num_kv_heads, g, HD) + 8 * c;
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) kf[pg][kk] = ld16(kb + 32 * kk);
+        for (int kk = 0; kk < C::KK; ++kk) B.k[pg][kk] = ld16(kb + 32 * kk);
 #pragma unroll
         for (int i = 0; i < C::VLD; ++i)
-          vf[pg][i] = ld16(value_pool + pool_row_offset(b, i * C::RPL + vrow_base, num_kv_heads, g, HD) + vcol);
+          B.v[pg][i] = ld16(value_pool + pool_row_offset(b, i * C::RPL + vrow_base, num_kv_heads, g, HD) + vcol);
       } else {
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) kf[pg][kk] = uint4{0, 0, 0, 0};
+        for (int kk = 0; kk < C::KK; ++kk) B.k[pg][kk] = uint4{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < C::VLD; ++i) vf[pg][i] = uint4{0, 0, 0, 0};
+        for (int i = 0; i < C::VLD; ++i) B.v[pg][i] = uint4{0, 0, 0, 0};
       }
     }
+  };
 
+  auto compute = [&](int u, const DecBuf<HD>& B) {
+    const int t0 = tok0 + 32 * u;
     // S^T = K Q^T for both blocks: lane (n, c) gets head n, tokens 4c .. 4c+3 of each block.
     floatx4 sacc[2];
 #pragma unroll
@@ -171,54 +193,56 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
       sacc[pg] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk)
-        sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[pg][kk]), qf[kk], sacc[pg], 0, 0, 0);
+        sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(B.k[pg][kk]), qf[kk], sacc[pg], 0, 0, 0);
     }
-
     // Stage V (rows at or past ctx become zero so that stale slots never reach the MFMA).
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int i = 0; i < C::VLD; ++i) {
         const int row = i * C::RPL + vrow_base;
-        const uint4 v = (t0 + pg * kBlockSize + row < ctx) ? vf[pg][i] : uint4{0, 0, 0, 0};
+        const uint4 v = (t0 + pg * kBlockSize + row < ctx) ? B.v[pg][i] : uint4{0, 0, 0, 0};
         st16(vstage + (pg * kBlockSize + row) * VP + vcol, v);
       }
-
-    // Online softmax over the 32 positions of this step (log2 domain).
-    float x[8];
+    // Online softmax (log2 domain, scale folded into the exponent's FMA).
     float mx = -INFINITY;
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
-      const bool blk_ok = (pg ? b1 : b0) >= 0;
+      const bool blk_ok = (pg ? B.b1 : B.b0) >= 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tok = t0 + pg * kBlockSize + 4 * c + j;
-        const float v = (blk_ok && tok < ctx) ? sacc[pg][j] * scale_log2 : -INFINITY;
-        x[pg * 4 + j] = v;
-        mx = fmaxf(mx, v);
+        sacc[pg][j] = (blk_ok && tok < ctx) ? sacc[pg][j] : -INFINITY;
+        mx = fmaxf(mx, sacc[pg][j]);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float m_tile = mx * scale_log2;
+    const bool need = m_tile > m_ref + kRescaleGap;
+    if (__any(need)) {
+      const float alpha = need ? fast_exp2(m_ref - m_tile) : 1.f;
+      m_ref = need ? m_tile : m_ref;
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) acc[mt] *= alpha;
+    }
+    // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
+    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
     float psum = 0.f;
     bf16x8 pb;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(x[e] - m_use);
-      psum += p;
-      pb[e] = static_cast<__bf16>(p);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) acc[mt] *= alpha;
+      for (int j = 0; j < 4; ++j) {
+        const float p = fast_exp2(__builtin_fmaf(sacc[pg][j], scale_log2, neg_m));
+        psum += p;
+        pb[4 * pg + j] = static_cast<__bf16>(p);
+      }
+    l_run += psum;
 
     // The staged rows are read back by this wave only; keep the compiler from moving reads up.
     __asm__ volatile("" ::: "memory");
-
     // O^T += V^T P^T.  A operand: lane (n, c) needs V[token 4c+e][d = 16mt + n] of both blocks.
     const uint16_t* r0 = vstage + (4 * c + (n >> 2)) * VP + 4 * (n & 3);
     const uint16_t* r1 = r0 + kBlockSize * VP;
@@ -228,6 +252,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[mt], 0, 0, 0);
     }
     __asm__ volatile("" ::: "memory");
+  };
+
+  DecBuf<HD> A, Bn;
+  int u = wave;
+  if (u < units) load(u, A);
+  if constexpr (kPrefetch) {
+    for (; u < units; u += 2 * kDecWaves) {
+      const int u2 = u + kDecWaves;
+      if (u2 < units) load(u2, Bn);
+      compute(u, A);
+      const int u3 = u2 + kDecWaves;
+      if (u3 < units) load(u3, A);
+      if (u2 < units) compute(u2, Bn);
+    }
+  } else {
+    for (; u < units; u += kDecWaves) {
+      if (u != wave) load(u, A);
+      compute(u, A);
+    }
   }
 
   // Normaliser of head n: sum the four lane groups.
@@ -241,11 +284,70 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
   for (int mt = 0; mt < C::MT; ++mt)
     *reinterpret_cast<floatx4*>(comb_o + (wave * kMaxGroup + n) * HD + 16 * mt + 4 * c) = acc[mt];
   if (c == 0) {
-    comb_ml[(wave * kMaxGroup + n) * 2] = m_run;
+    comb_ml[(wave * kMaxGroup + n) * 2] = m_ref;
     comb_ml[(wave * kMaxGroup + n) * 2 + 1] = l_run;
   }
   __syncthreads();
-  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16);
+  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, A_.max_splits, num_q_heads, A_.ws_o, A_.ws_ml, A_.out,
+                  A_.out_bf16);
+}
+
+// Persistent form: a fixed grid walks the compact list of work items.  Items are numbered in
+// order of (sequence, split, KV head), each sequence contributing max(1, ceil(ctx / split)) x Hkv of
+// them; workgroup b takes items b, b + gridDim.x, ...  Every workgroup rebuilds the numbering from
+// context_lens with a block-wide prefix sum over 256 sequences at a time, so the host never needs
+// the lengths and no workgroup is launched without work.  With gridDim.x a multiple of 8 and
+// Hkv = 8, KV head g always lands on the same XCD (workgroups are dealt round-robin over the 8
+// XCDs), so blocks shared between sequences stay in that XCD's L2.
+template <int HD, bool CHECK>
+__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, int num_seqs) {
+  __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
+  __shared__ int pref[kDecThreads];
+  const int tid = threadIdx.x;
+  const int stride = gridDim.x;
+  int next = blockIdx.x;
+  int base = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += kDecThreads) {
+    const int sq = c0 + tid;
+    int cnt = 0;
+    if (sq < num_seqs) {
+      const int ctx = clamp_ctx<CHECK>(a.context_lens[sq], a.max_blocks, a.err_flag, blockIdx.x == 0);
+      cnt = (ctx == 0 ? 1 : (ctx + a.split_tokens - 1) / a.split_tokens) * a.num_kv_heads;
+    }
+    __syncthreads();  // the previous chunk's searches are done with pref
+    pref[tid] = cnt;
+    __syncthreads();
+#pragma unroll
+    for (int off = 1; off < kDecThreads; off <<= 1) {
+      const int v = tid >= off ? pref[tid - off] : 0;
+      __syncthreads();
+      pref[tid] += v;
+      __syncthreads();
+    }
+    const int chunk_total = pref[kDecThreads - 1];
+    while (next < base + chunk_total) {
+      const int local = next - base;
+      int lo = 0, hi = kDecThreads - 1;  // first j with pref[j] > local
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] > local) hi = mid; else lo = mid + 1;
+      }
+      const int s = c0 + lo;
+      const int r = local - (lo ? pref[lo - 1] : 0);
+      const int split = r / a.num_kv_heads, g = r - split * a.num_kv_heads;
+      const int ctx = clamp_ctx<CHECK>(a.context_lens[s], a.max_blocks, a.err_flag, false);
+      if (ctx == 0) {
+        for (int i = tid; i < a.group * HD; i += kDecThreads)
+          store_out(a.out, (static_cast<int64_t>(s) * a.num_q_heads + g * a.group) * HD + i, 0.f, a.out_bf16);
+      } else {
+        const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+        decode_bf16_item<HD, CHECK, false>(a, s, g, split, ctx, nsplit, smem);
+      }
+      __syncthreads();  // the next item reuses the staging and merge areas
+      next += stride;
+    }
+    base += chunk_total;
+  }
 }
 
 // fp32 pools: VALU kernel.  A wave step covers 32 positions; lanes 0-31 and 32-63 each take one
@@ -410,7 +512,7 @@ int env_split_tokens() {
     const char* e = std::getenv("PKV_SPLIT_TOKENS");
     if (!e) return 0;
     const int x = std::atoi(e);
-    return (x > 0 && x % 128 == 0) ? x : 0;
+    return (x > 0 && x % 128 == 0 && x <= 1024) ? x : 0;
   }();
   return v;
 }
@@ -439,16 +541,17 @@ extern "C" int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 512;
   const int64_t max_ctx = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
   const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  // Prefer long splits (fewer partials) while the grid still offers several workgroups per CU.
-  if (pairs * ((max_ctx + 511) / 512) >= 1024) return 512;
-  if (pairs * ((max_ctx + 255) / 256) >= 512) return 256;
+  // Prefer long splits (fewer partials, fewer merges) while the largest possible number of work
+  // items still fills two workgroups per CU.
+  for (int S : {1024, 512, 256})
+    if (pairs * ((max_ctx + S - 1) / S) >= 512) return S;
   return 128;
 }
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq, int32_t split_tokens) {
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 0;
-  if (split_tokens < 0 || split_tokens % 128 != 0) return 0;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 1024) return 0;
   const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
   const int64_t max_splits = (static_cast<int64_t>(max_blocks_per_seq) * kBlockSize + S - 1) / S;
   if (max_splits <= 1) return 0;
@@ -464,7 +567,8 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
                                             int32_t* err_flag, void* stream) {
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
     return PKV_ERR_INVALID_ARG;
-  if (split_tokens < 0 || split_tokens % 128 != 0 || !std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 1024) return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return PKV_ERR_UNSUPPORTED;
   if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
@@ -500,7 +604,22 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
     default: PKV_DEC(KERNEL, T, 256, CHECK); break;  \
   }
   if (dtype == PKV_DTYPE_BF16) {
-    if (err_flag) { PKV_DEC_HD(decode_bf16_kernel, uint16_t, true) } else { PKV_DEC_HD(decode_bf16_kernel, uint16_t, false) }
+    DecArgs a{static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_pool),
+              static_cast<const uint16_t*>(value_pool), block_tables, context_lens, ws_o, ws_ml, out, err_flag,
+              max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, max_splits, ob, scale_log2};
+    // Two resident workgroups per CU at head_dim <= 128 (register bound), one at 256; never more
+    // workgroups than the largest possible number of items.
+    const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * max_splits;
+    const int64_t resident = static_cast<int64_t>(pkv_host::cu_count()) * (head_dim <= 128 ? 2 : 1);
+    const dim3 pgrid(static_cast<unsigned>(max_items < resident ? max_items : resident));
+#define PKV_DEC_BF16(HD, CHECK) \
+  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK>), pgrid, dim3(kDecThreads), 0, st, a, num_seqs)
+    switch (head_dim) {
+      case 64: if (err_flag) PKV_DEC_BF16(64, true); else PKV_DEC_BF16(64, false); break;
+      case 128: if (err_flag) PKV_DEC_BF16(128, true); else PKV_DEC_BF16(128, false); break;
+      default: if (err_flag) PKV_DEC_BF16(256, true); else PKV_DEC_BF16(256, false); break;
+    }
+#undef PKV_DEC_BF16
   } else {
     if (err_flag) { PKV_DEC_HD(decode_f32_kernel, float, true) } else { PKV_DEC_HD(decode_f32_kernel, float, false) }
   }

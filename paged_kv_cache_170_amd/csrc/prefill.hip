@@ -10,11 +10,17 @@
 //     workgroup id is remapped so that each XCD (workgroups are dealt round-robin over the 8 XCDs)
 //     gets a contiguous run of items, i.e. the query heads of one KV head, which then share that
 //     KV head's K/V stream in the XCD's L2.
-//   * 4 waves x 32 query rows.  Key tiles of 64 positions (4 blocks) are gathered through the
-//     block table into LDS (register prefetch of the next tile overlaps the current tile's math).
+//   * 8 waves in two groups of four; each wave owns 32 query rows, and the two groups split the
+//     key range (even and odd key tiles), so every SIMD runs two independent waves whose MFMA and
+//     softmax work overlap.  The groups' (o, m, l) states are merged in LDS at the end.
+//   * key tiles (64 positions = 4 blocks; 32 for head_dim 256) are gathered through the block
+//     table by all 512 threads, a pair at a time, into double-buffered LDS; the next pair's loads
+//     are in flight while the current pair is computed, with one barrier per pair.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows in registers);
 //     the accumulator layout gives each lane 16 keys of one query, so the row max needs one
-//     cross-lane step.  The causal mask is an absolute-position compare.
+//     cross-lane step.  Only tiles crossing the causal diagonal or the key end are masked, and the
+//     running max is moved lazily (only when a tile max exceeds it by 2^8), which keeps the
+//     accumulator rescale off the common path.
 //   * P stays in registers and is exactly the B operand of O^T = V^T P^T; V^T comes from the
 //     natural-layout V tile through ds_read_b64_tr_b16.
 #include <cmath>
@@ -23,21 +29,28 @@
 
 namespace pkv {
 
-constexpr int kPreWaves = 4;
+constexpr int kPreWaves = 8;                    // two groups of four waves
 constexpr int kPreThreads = kPreWaves * kWave;
-constexpr int kPreRows = 32;                        // query rows per wave
-constexpr int kPreTile = kPreWaves * kPreRows;      // query rows per workgroup
-constexpr int kKeyTile = 64;                        // key positions per LDS tile
+constexpr int kPreRows = 32;                    // query rows per wave
+constexpr int kPreTile = 4 * kPreRows;          // query rows per workgroup
+constexpr float kRescaleGap = 8.f;              // log2 units the running max may trail the tile max
 
 template <int HD>
 struct PreCfg {
-  static constexpr int KS = HD / 16;           // k-steps of S^T over head_dim
-  static constexpr int MD = HD / 32;           // 32-row tiles of O^T
-  static constexpr int KPITCH = HD * 2 + 16;   // LDS bytes per K row
-  static constexpr int VPITCH = HD * 2 + 32;   // LDS bytes per V row
-  static constexpr int CPR = HD / 8;           // 16-byte chunks per row
-  static constexpr int LOADS = kKeyTile * CPR / kPreThreads;  // chunks per thread per tensor per tile
-  static constexpr int LDS = kKeyTile * (KPITCH + VPITCH);
+  static constexpr int KT = HD == 256 ? 32 : 64;  // key positions per LDS tile
+  static constexpr int MS = KT / 32;              // 32-key row tiles of S^T
+  static constexpr int KA = KT / 16;              // 16-key k-steps of O^T
+  static constexpr int KS = HD / 16;              // k-steps of S^T over head_dim
+  static constexpr int MD = HD / 32;              // 32-row tiles of O^T
+  static constexpr int KPITCH = HD * 2 + 16;      // LDS bytes per K row (conflict-free 16-byte reads)
+  static constexpr int VPITCH = HD * 2 + 32;      // LDS bytes per V row (conflict-free transposed reads)
+  static constexpr int CPR = HD / 8;              // 16-byte chunks per row
+  static constexpr int TILE = KT * (KPITCH + VPITCH);
+  static constexpr int LOADS = 2 * KT * CPR / kPreThreads;  // chunks per thread per tensor per tile pair
+  static constexpr int LDS = 4 * TILE;                       // two buffers of a tile pair
+  static constexpr int COMB = 4 * kPreRows * HD * 4 + 2 * 4 * kPreRows * 4;
+  static_assert(LDS >= COMB, "merge area must fit in the tile buffers");
+  static_assert(LOADS * kPreThreads == 2 * KT * CPR, "pair loads must divide evenly");
 };
 
 template <int HD, bool CHECK>
@@ -49,8 +62,6 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     void* __restrict__ out, int out_bf16, int32_t* err_flag) {
   using C = PreCfg<HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  char* k_lds = smem;
-  char* v_lds = smem + kKeyTile * C::KPITCH;
 
   // Work item: XCD-contiguous remap of the linear workgroup id.
   const int items = gridDim.x, id = blockIdx.x;
@@ -75,8 +86,9 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
   const int kv_end = causal ? off + min(row0 + kPreTile, L) : off + L;
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int grp = wave >> 2, wq = wave & 3;  // group grp takes key tiles grp, grp + 2, ...
   const int qc = lane & 31, hh = lane >> 5;
-  const int wrow0 = row0 + wave * kPreRows;
+  const int wrow0 = row0 + wq * kPreRows;
   const int myrow = wrow0 + qc;
   const bool row_ok = myrow < L;
   const int qpos = off + myrow;
@@ -95,15 +107,18 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
   for (int md = 0; md < C::MD; ++md)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[md][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
+  // Tile pair p holds key tiles 2p and 2p+1; all 512 threads gather it through the block table.
   uint4 kreg[C::LOADS], vreg[C::LOADS];
-  auto load_tile = [&](int kt) {
+  auto load_pair = [&](int p) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int f = threadIdx.x + kPreThreads * i;
-      const int row = f / C::CPR, col = (f % C::CPR) * 8;
-      const int key = kt * kKeyTile + row;
+      const int tt = f / (C::KT * C::CPR);
+      const int rem = f - tt * (C::KT * C::CPR);
+      const int row = rem / C::CPR, col = (rem % C::CPR) * 8;
+      const int key = (2 * p + tt) * C::KT + row;
       uint4 kv = uint4{0, 0, 0, 0}, vv = uint4{0, 0, 0, 0};
       if (key < kv_end) {
         const int b = load_block_id<CHECK>(table, key / kBlockSize, num_blocks, err_flag);
@@ -117,96 +132,146 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       vreg[i] = vv;
     }
   };
-
-  const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
-  load_tile(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // the previous tile's readers are done
+  auto store_pair = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int f = threadIdx.x + kPreThreads * i;
-      const int row = f / C::CPR, col = (f % C::CPR) * 8;
-      st16(k_lds + row * C::KPITCH + col * 2, kreg[i]);
-      st16(v_lds + row * C::VPITCH + col * 2, vreg[i]);
+      const int tt = f / (C::KT * C::CPR);
+      const int rem = f - tt * (C::KT * C::CPR);
+      const int row = rem / C::CPR, col = (rem % C::CPR) * 8;
+      char* base = smem + (2 * buf + tt) * C::TILE;
+      st16(base + row * C::KPITCH + col * 2, kreg[i]);
+      st16(base + C::KT * C::KPITCH + row * C::VPITCH + col * 2, vreg[i]);
     }
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+  };
 
-    const int key0 = kt * kKeyTile;
-    const bool active = wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
+  const int ntiles = (kv_end + C::KT - 1) / C::KT;
+  const int npairs = (ntiles + 1) / 2;
+  load_pair(0);
+  store_pair(0);
+  __syncthreads();
+
+  const int li = lane & 15, dg = (lane >> 4) & 1;
+  constexpr int VP = C::VPITCH / 2;
+  for (int pr = 0; pr < npairs; ++pr) {
+    const int cur = pr & 1;
+    if (pr + 1 < npairs) load_pair(pr + 1);
+    const int kt = 2 * pr + grp;
+    const int key0 = kt * C::KT;
+    const bool active = kt < ntiles && wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
     if (active) {
-      floatx16 sacc[2];
+      const char* tile = smem + (2 * cur + grp) * C::TILE;
+      floatx16 sacc[C::MS];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int ms = 0; ms < C::MS; ++ms) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-        const char* krow = k_lds + (32 * mt + qc) * C::KPITCH + 16 * hh;
+        for (int e = 0; e < 16; ++e) sacc[ms][e] = 0.f;
+        const char* krow = tile + (32 * ms + qc) * C::KPITCH + 16 * hh;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
-          sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+          sacc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[ms], 0, 0, 0);
         }
       }
-      // Element e = 4i + j of sacc[mt] is key key0 + 32mt + 8i + 4hh + j for query row qc.
+      // Element e = 4i + j of sacc[ms] is key key0 + 32ms + 8i + 4hh + j for query row qc.  Only
+      // tiles that cross the causal diagonal or the end of the keys need the mask.
+      const bool edge = key0 + C::KT > kv_end || (causal && key0 + C::KT - 1 > off + wrow0);
+      if (edge) {
+#pragma unroll
+        for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + 32 * ms + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const bool ok = key < kv_end && (!causal || key <= qpos);
+            sacc[ms][e] = ok ? sacc[ms][e] : -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = key0 + 32 * mt + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const bool ok = key < kv_end && (!causal || key <= qpos);
-          const float v = ok ? sacc[mt][e] * scale_log2 : -INFINITY;
-          sacc[mt][e] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[ms][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-      bf16x8 pb[4];
+      // Lazy rescale: the reference max moves only when the tile max exceeds it by kRescaleGap,
+      // so probabilities stay below 2^kRescaleGap and the accumulators are rarely touched.
+      const float m_tile = mx * scale_log2;
+      const bool need = m_tile > m_ref + kRescaleGap;
+      if (__any(need)) {
+        const float alpha = need ? fast_exp2(m_ref - m_tile) : 1.f;
+        m_ref = need ? m_tile : m_ref;
+        l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int md = 0; md < C::MD; ++md) acc[md] *= alpha;
+      }
+      // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
+      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+      float psum = 0.f;
+      bf16x8 pb[C::KA];
+#pragma unroll
+      for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(sacc[mt][e] - m_use);
+          const float p = fast_exp2(__builtin_fmaf(sacc[ms][e], scale_log2, neg_m));
           psum += p;
-          pb[2 * mt + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+          pb[2 * ms + (e >> 3)][e & 7] = static_cast<__bf16>(p);
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int md = 0; md < C::MD; ++md) acc[md] *= alpha;
+      l_run += psum;
 
       // O^T += V^T P^T.  k-step a covers keys 16a + 4hh + e and 16a + 8 + 4hh + e (e = 0..3),
       // matching pb[a]; the A operand lane (l % 32 = d, hh) reads those keys' V at d.
-      const int li = lane & 15, dg = (lane >> 4) & 1;
-      const uint16_t* vbase = reinterpret_cast<const uint16_t*>(v_lds);
-      constexpr int VP = C::VPITCH / 2;
+      const uint16_t* vbase = reinterpret_cast<const uint16_t*>(tile + C::KT * C::KPITCH);
 #pragma unroll
       for (int md = 0; md < C::MD; ++md) {
         const int col = 32 * md + 16 * dg + 4 * (li & 3);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < C::KA; ++a) {
           const int r0 = 16 * a + 4 * hh + (li >> 2);
           const bf16x8 av = concat(lds_read_tr16(vbase + r0 * VP + col), lds_read_tr16(vbase + (r0 + 8) * VP + col));
           acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[a], acc[md], 0, 0, 0);
         }
       }
     }
+    if (pr + 1 < npairs) store_pair(cur ^ 1);
+    __syncthreads();
   }
 
+  // Merge the two key groups: group 1 parks its state in LDS, group 0 combines and writes.
   l_run += __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  float* co = reinterpret_cast<float*>(smem);
+  float* cm = co + 4 * kPreRows * HD;
+  float* cl = cm + 4 * kPreRows;
+  if (grp == 1) {
+#pragma unroll
+    for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * md + 8 * i + 4 * hh;
+        *reinterpret_cast<float4*>(co + (wq * kPreRows + qc) * HD + d) =
+            float4{acc[md][4 * i], acc[md][4 * i + 1], acc[md][4 * i + 2], acc[md][4 * i + 3]};
+      }
+    if (hh == 0) {
+      cm[wq * kPreRows + qc] = m_ref;
+      cl[wq * kPreRows + qc] = l_run;
+    }
+  }
+  __syncthreads();
+  if (grp == 1 || !row_ok) return;
+  const float mb = cm[wq * kPreRows + qc], lb = cl[wq * kPreRows + qc];
+  const float M = fmaxf(m_ref, mb);
+  const float fa = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - M);
+  const float fb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - M);
+  const float Ls = fa * l_run + fb * lb;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  const float ia = fa * inv, ib = fb * inv;
   const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
 #pragma unroll
   for (int md = 0; md < C::MD; ++md)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * md + 8 * i + 4 * hh;
-      const float v0 = acc[md][4 * i] * inv, v1 = acc[md][4 * i + 1] * inv, v2 = acc[md][4 * i + 2] * inv,
-                  v3 = acc[md][4 * i + 3] * inv;
+      const float4 ob = *reinterpret_cast<const float4*>(co + (wq * kPreRows + qc) * HD + d);
+      const float v0 = acc[md][4 * i] * ia + ob.x * ib, v1 = acc[md][4 * i + 1] * ia + ob.y * ib,
+                  v2 = acc[md][4 * i + 2] * ia + ob.z * ib, v3 = acc[md][4 * i + 3] * ia + ob.w * ib;
       if (out_bf16) {
         uint16_t* o = static_cast<uint16_t*>(out) + obase + d;
         const uint2 pk = uint2{static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
@@ -231,7 +296,7 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
                                                    int32_t causal, float scale, pkv_dtype dtype, int32_t* err_flag,
                                                    void* stream) {
   if (num_seqs < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
-      num_kv_heads <= 0 || !std::isfinite(scale))
+      num_kv_heads <= 0 || !std::isfinite(scale) || !(scale > 0.f))
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
@@ -248,7 +313,8 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
 #define PKV_PRE(HD, CHECK)                                                                                      \
-  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK>), dim3(static_cast<unsigned>(items)), dim3(kPreThreads), 0, \
+  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK>), dim3(static_cast<unsigned>(items)), dim3(kPreThreads),    \
+                     0,                                                                                         \
                      st, static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets,                         \
                      static_cast<const uint16_t*>(key_pool), static_cast<const uint16_t*>(value_pool),           \
                      block_tables, max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks,    \
