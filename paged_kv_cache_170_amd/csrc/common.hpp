@@ -45,6 +45,13 @@ __device__ __forceinline__ int load_block_id(const int32_t* table_row, int j, in
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte load marked non-temporal: for data read once (streamed through the caches).
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+}
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -68,7 +75,21 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* lds_ptr) {
 }
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float floatx2;
+
+// Two fp32 values to a packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{a, b}), bf16x2));
+}
+
+// acc + lo + hi of a packed bf16 pair, accumulated in fp32 (one v_dot2c_f32_bf16 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
 }
 
 }  // namespace pkv

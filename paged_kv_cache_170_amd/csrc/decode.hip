@@ -11,10 +11,11 @@
 //     device from context_lens, so no workgroup is launched idle); a workgroup of 4 waves owns
 //     `split_tokens` positions of one (sequence, KV head) and serves all G query heads of that
 //     group from each loaded page.
-//   * a wave step covers 32 positions = two 16-token blocks.  K is loaded straight into MFMA
-//     operand registers; S^T = K Q^T uses v_mfma_f32_16x16x32_bf16 with the 16 MFMA columns
-//     holding the G query heads (zero-padded).  V rows are staged in LDS in their natural layout
-//     and read back transposed with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T.
+//   * a wave step covers 32 positions = two 16-token blocks.  K and V rows are fetched whole
+//     (every wave-wide load covers complete rows of the KV head) and staged in LDS;
+//     S^T = K Q^T uses v_mfma_f32_16x16x32_bf16 with the 16 MFMA columns holding the G query
+//     heads (zero-padded), and V is read back transposed with ds_read_b64_tr_b16 as the A operand
+//     of O^T = V^T P^T.
 //   * the online softmax runs in the log2 domain on the MFMA accumulator layout; the 4 waves'
 //     states merge in LDS, and a split's (o, m, l) goes to the workspace unless the sequence
 //     fits one split, in which case the normalised row is written directly.
@@ -35,12 +36,13 @@ template <int HD>
 struct DecCfg {
   static constexpr int KK = HD / 32;          // k-steps of S^T = K Q^T over head_dim
   static constexpr int MT = HD / 16;          // 16-row tiles of O^T
-  static constexpr int VPITCH = HD * 2 + 32;  // bytes per staged V row (keeps transposed reads conflict-free)
-  static constexpr int LPR = HD / 8;          // lanes per V row in a 16-byte-per-lane load
-  static constexpr int RPL = kWave / LPR;     // V rows per wave-wide load
-  static constexpr int VLD = kBlockSize / RPL;  // wave-wide loads per block
-  static constexpr int STAGE = 2 * kBlockSize * VPITCH;  // bytes per wave
-  static constexpr int COMB = kMaxGroup * HD * 4;        // bytes per wave for the merge
+  static constexpr int KPITCH = HD * 2 + 16;  // bytes per staged K row (conflict-free 16-byte reads)
+  static constexpr int VPITCH = HD * 2 + 32;  // bytes per staged V row (conflict-free transposed reads)
+  static constexpr int LPR = HD / 8;          // lanes per row in a 16-byte-per-lane load
+  static constexpr int RPL = kWave / LPR;     // rows per wave-wide load
+  static constexpr int VLD = kBlockSize / RPL;  // wave-wide loads per block and tensor
+  static constexpr int STAGE = 2 * kBlockSize * (KPITCH + VPITCH);  // bytes per wave (two blocks of K and V)
+  static constexpr int COMB = kMaxGroup * HD * 4;                   // bytes per wave for the merge
   static constexpr int BODY = (STAGE > COMB ? STAGE : COMB) * kDecWaves;
   static constexpr int LDS = BODY + kDecWaves * kMaxGroup * 2 * 4;
 };
@@ -112,25 +114,24 @@ struct DecArgs {
 
 template <int HD>
 struct DecBuf {
-  uint4 k[2][DecCfg<HD>::KK];
+  uint4 k[2][DecCfg<HD>::VLD];
   uint4 v[2][DecCfg<HD>::VLD];
   int b0, b1;
 };
 
 // One work item: positions [split * split_tokens, min(+split_tokens, ctx)) of sequence s, KV head g,
 // for all query heads of the group.  Called by all 256 threads of the workgroup.
-template <int HD, bool CHECK, bool PREFETCH>
+template <int HD, bool CHECK>
 __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g, int split, int ctx, int nsplit,
                                                  char* smem) {
   using C = DecCfg<HD>;
-  const uint16_t* __restrict__ query = A_.query;
   const uint16_t* __restrict__ key_pool = A_.key_pool;
   const uint16_t* __restrict__ value_pool = A_.value_pool;
   const int num_q_heads = A_.num_q_heads, num_kv_heads = A_.num_kv_heads, group = A_.group;
   const int num_blocks = A_.num_blocks, split_tokens = A_.split_tokens;
   const float scale_log2 = A_.scale_log2;
   int32_t* err_flag = A_.err_flag;
-  constexpr bool kPrefetch = PREFETCH;
+
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, c = lane >> 4;
   const int tok0 = split * split_tokens;
@@ -145,7 +146,8 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
   bf16x8 qf[C::KK];
   {
     const bool live = n < group;
-    const uint16_t* qrow = query + (static_cast<int64_t>(s) * num_q_heads + g * group + (live ? n : 0)) * HD + 8 * c;
+    const uint16_t* qrow =
+        A_.query + (static_cast<int64_t>(s) * num_q_heads + g * group + (live ? n : 0)) * HD + 8 * c;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
   }
@@ -155,12 +157,13 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* vstage = reinterpret_cast<uint16_t*>(smem + wave * C::STAGE);
-  constexpr int VP = C::VPITCH / 2;  // pitch in elements
+  char* kstage = smem + wave * C::STAGE;                      // [32 rows][KPITCH]
+  char* vstage = kstage + 2 * kBlockSize * C::KPITCH;         // [32 rows][VPITCH]
   const int units = (tok_end - tok0 + 31) / 32;
-  const int vrow_base = lane / C::LPR, vcol = (lane % C::LPR) * 8;
+  const int row_base = lane / C::LPR, col = (lane % C::LPR) * 8;
 
-  // Step u covers positions tok0 + 32u .. +31 (two blocks).  Issue all of its loads.
+  // Step u covers positions tok0 + 32u .. +31 (two blocks).  K and V rows are read whole (each
+  // wave-wide load covers RPL complete rows) and staged in LDS in their natural layout.
   auto load = [&](int u, DecBuf<HD>& B) {
     const int t0 = tok0 + 32 * u;
     B.b0 = __builtin_amdgcn_readlane(my_id, 2 * u);
@@ -168,42 +171,45 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       const int b = pg ? B.b1 : B.b0;
-      if (b >= 0) {
-        const uint16_t* kb = key_pool + pool_row_offset(b, n, num_kv_heads, g, HD) + 8 * c;
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) B.k[pg][kk] = ld16(kb + 32 * kk);
-#pragma unroll
-        for (int i = 0; i < C::VLD; ++i)
-          B.v[pg][i] = ld16(value_pool + pool_row_offset(b, i * C::RPL + vrow_base, num_kv_heads, g, HD) + vcol);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) B.k[pg][kk] = uint4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < C::VLD; ++i) B.v[pg][i] = uint4{0, 0, 0, 0};
+      for (int i = 0; i < C::VLD; ++i) {
+        if (b >= 0) {
+          const int64_t o = pool_row_offset(b, i * C::RPL + row_base, num_kv_heads, g, HD) + col;
+          B.k[pg][i] = ld16(key_pool + o);
+          B.v[pg][i] = ld16(value_pool + o);
+        } else {
+          B.k[pg][i] = uint4{0, 0, 0, 0};
+          B.v[pg][i] = uint4{0, 0, 0, 0};
+        }
       }
     }
   };
 
   auto compute = [&](int u, const DecBuf<HD>& B) {
     const int t0 = tok0 + 32 * u;
-    // S^T = K Q^T for both blocks: lane (n, c) gets head n, tokens 4c .. 4c+3 of each block.
-    floatx4 sacc[2];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      sacc[pg] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk)
-        sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(B.k[pg][kk]), qf[kk], sacc[pg], 0, 0, 0);
-    }
-    // Stage V (rows at or past ctx become zero so that stale slots never reach the MFMA).
+    // Stage K and V (V rows at or past ctx become zero so stale slots never reach the MFMA).
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int i = 0; i < C::VLD; ++i) {
-        const int row = i * C::RPL + vrow_base;
-        const uint4 v = (t0 + pg * kBlockSize + row < ctx) ? B.v[pg][i] : uint4{0, 0, 0, 0};
-        st16(vstage + (pg * kBlockSize + row) * VP + vcol, v);
+        const int row = pg * kBlockSize + i * C::RPL + row_base;
+        st16(kstage + row * C::KPITCH + col * 2, B.k[pg][i]);
+        st16(vstage + row * C::VPITCH + col * 2, (t0 + row < ctx) ? B.v[pg][i] : uint4{0, 0, 0, 0});
       }
+    // The staged rows are read back by this wave only; keep the compiler from moving reads up.
+    __asm__ volatile("" ::: "memory");
+    // S^T = K Q^T for both blocks: lane (n, c) gets head n, tokens 4c .. 4c+3 of each block.
+    floatx4 sacc[2];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const char* krow = kstage + (pg * kBlockSize + n) * C::KPITCH + 16 * c;
+      sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(krow), qf[0],
+                                                         floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < C::KK; ++kk)
+        sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(krow + 64 * kk), qf[kk],
+                                                           sacc[pg], 0, 0, 0);
+    }
     // Online softmax (log2 domain, scale folded into the exponent's FMA).
     float mx = -INFINITY;
 #pragma unroll
@@ -227,25 +233,23 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) acc[mt] *= alpha;
     }
-    // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
+    // A head that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
     const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-    float psum = 0.f;
-    bf16x8 pb;
+    uint32_t pw[4];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[pg][j], scale_log2, neg_m));
-        psum += p;
-        pb[4 * pg + j] = static_cast<__bf16>(p);
+      for (int q = 0; q < 2; ++q) {
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[pg][2 * q], scale_log2, neg_m));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[pg][2 * q + 1], scale_log2, neg_m));
+        pw[2 * pg + q] = pack_bf16x2(p0, p1);
       }
-    l_run += psum;
+    l_run = add_bf16x2(pw[0], add_bf16x2(pw[1], add_bf16x2(pw[2], add_bf16x2(pw[3], l_run))));
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, uint4{pw[0], pw[1], pw[2], pw[3]});
 
-    // The staged rows are read back by this wave only; keep the compiler from moving reads up.
-    __asm__ volatile("" ::: "memory");
     // O^T += V^T P^T.  A operand: lane (n, c) needs V[token 4c+e][d = 16mt + n] of both blocks.
-    const uint16_t* r0 = vstage + (4 * c + (n >> 2)) * VP + 4 * (n & 3);
-    const uint16_t* r1 = r0 + kBlockSize * VP;
+    const uint16_t* r0 = reinterpret_cast<const uint16_t*>(vstage + (4 * c + (n >> 2)) * C::VPITCH) + 4 * (n & 3);
+    const uint16_t* r1 = r0 + kBlockSize * (C::VPITCH / 2);
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) {
       const bf16x8 a = concat(lds_read_tr16(r0 + 16 * mt), lds_read_tr16(r1 + 16 * mt));
@@ -254,23 +258,10 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
     __asm__ volatile("" ::: "memory");
   };
 
-  DecBuf<HD> A, Bn;
-  int u = wave;
-  if (u < units) load(u, A);
-  if constexpr (kPrefetch) {
-    for (; u < units; u += 2 * kDecWaves) {
-      const int u2 = u + kDecWaves;
-      if (u2 < units) load(u2, Bn);
-      compute(u, A);
-      const int u3 = u2 + kDecWaves;
-      if (u3 < units) load(u3, A);
-      if (u2 < units) compute(u2, Bn);
-    }
-  } else {
-    for (; u < units; u += kDecWaves) {
-      if (u != wave) load(u, A);
-      compute(u, A);
-    }
+  DecBuf<HD> A;
+  for (int u = wave; u < units; u += kDecWaves) {
+    load(u, A);
+    compute(u, A);
   }
 
   // Normaliser of head n: sum the four lane groups.
@@ -341,7 +332,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, int
           store_out(a.out, (static_cast<int64_t>(s) * a.num_q_heads + g * a.group) * HD + i, 0.f, a.out_bf16);
       } else {
         const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-        decode_bf16_item<HD, CHECK, false>(a, s, g, split, ctx, nsplit, smem);
+        decode_bf16_item<HD, CHECK>(a, s, g, split, ctx, nsplit, smem);
       }
       __syncthreads();  // the next item reuses the staging and merge areas
       next += stride;
@@ -477,28 +468,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_f32_kernel(
   merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16);
 }
 
-// Log-sum-exp merge of split partials: grid (num_q_heads, num_seqs), one thread per head_dim element.
+// Log-sum-exp merge of split partials: grid (num_kv_heads, num_seqs); the 256 threads cover the
+// group's query heads x head_dim.  Sequences that fit one split were finished by the main kernel.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_ml,
                                                             const int32_t* __restrict__ context_lens, int max_blocks,
-                                                            int num_q_heads, int head_dim, int split_tokens,
-                                                            int max_splits, void* __restrict__ out, int out_bf16) {
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+                                                            int num_q_heads, int group, int head_dim,
+                                                            int split_tokens, int max_splits, void* __restrict__ out,
+                                                            int out_bf16) {
+  const int g = blockIdx.x, s = blockIdx.y;
   int ctx = context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > max_blocks * kBlockSize ? max_blocks * kBlockSize : ctx);
   const int nsplit = (ctx + split_tokens - 1) / split_tokens;
-  if (nsplit <= 1 || d >= head_dim) return;
-  const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_splits;
-  float M = -INFINITY;
-  for (int p = 0; p < nsplit; ++p) M = fmaxf(M, ws_ml[(base + p) * 2]);
-  float O = 0.f, L = 0.f;
-  for (int p = 0; p < nsplit; ++p) {
-    const float mp = ws_ml[(base + p) * 2];
-    const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
-    O += f * ws_o[(base + p) * head_dim + d];
-    L += f * ws_ml[(base + p) * 2 + 1];
+  if (nsplit <= 1) return;
+  for (int i = threadIdx.x; i < group * head_dim; i += blockDim.x) {
+    const int h = g * group + i / head_dim, d = i % head_dim;
+    const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_splits;
+    float M = -INFINITY;
+    for (int p = 0; p < nsplit; ++p) M = fmaxf(M, ws_ml[(base + p) * 2]);
+    float O = 0.f, L = 0.f;
+#pragma unroll 4
+    for (int p = 0; p < nsplit; ++p) {
+      const float mp = ws_ml[(base + p) * 2];
+      const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
+      O += f * ws_o[(base + p) * head_dim + d];
+      L += f * ws_ml[(base + p) * 2 + 1];
+    }
+    store_out(out, (static_cast<int64_t>(s) * num_q_heads + h) * head_dim + d, L > 0.f ? O / L : 0.f, out_bf16 != 0);
   }
-  store_out(out, (static_cast<int64_t>(s) * num_q_heads + h) * head_dim + d, L > 0.f ? O / L : 0.f, out_bf16 != 0);
 }
 
 }  // namespace pkv
@@ -627,8 +624,8 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
 #undef PKV_DEC
   if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
   if (max_splits > 1) {
-    hipLaunchKernelGGL(decode_reduce_kernel, dim3(num_q_heads, num_seqs), dim3(head_dim), 0, st, ws_o, ws_ml,
-                       context_lens, max_blocks_per_seq, num_q_heads, head_dim, S, max_splits, out, ob);
+    hipLaunchKernelGGL(decode_reduce_kernel, dim3(num_kv_heads, num_seqs), dim3(256), 0, st, ws_o, ws_ml,
+                       context_lens, max_blocks_per_seq, num_q_heads, group, head_dim, S, max_splits, out, ob);
     return pkv_host::launch_status();
   }
   return PKV_OK;

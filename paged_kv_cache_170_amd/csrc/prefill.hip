@@ -34,6 +34,7 @@ constexpr int kPreThreads = kPreWaves * kWave;
 constexpr int kPreRows = 32;                    // query rows per wave
 constexpr int kPreTile = 4 * kPreRows;          // query rows per workgroup
 constexpr float kRescaleGap = 8.f;              // log2 units the running max may trail the tile max
+constexpr int kIdWindow = 2048;                 // block ids held in LDS (32,768 positions)
 
 template <int HD>
 struct PreCfg {
@@ -48,6 +49,7 @@ struct PreCfg {
   static constexpr int TILE = KT * (KPITCH + VPITCH);
   static constexpr int LOADS = 2 * KT * CPR / kPreThreads;  // chunks per thread per tensor per tile pair
   static constexpr int LDS = 4 * TILE;                       // two buffers of a tile pair
+  static constexpr int LINES = 2 * KT * (HD * 2 / 128);      // 128-byte lines per tensor per tile pair
   static constexpr int COMB = 4 * kPreRows * HD * 4 + 2 * 4 * kPreRows * 4;
   static_assert(LDS >= COMB, "merge area must fit in the tile buffers");
   static_assert(LOADS * kPreThreads == 2 * KT * CPR, "pair loads must divide evenly");
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     void* __restrict__ out, int out_bf16, int32_t* err_flag) {
   using C = PreCfg<HD>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ int ids[kIdWindow];  // block ids of logical blocks [win0, win0 + kIdWindow)
 
   // Work item: XCD-contiguous remap of the linear workgroup id.
   const int items = gridDim.x, id = blockIdx.x;
@@ -109,9 +112,20 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     for (int e = 0; e < 16; ++e) acc[md][e] = 0.f;
   float m_ref = -INFINITY, l_run = 0.f;
 
+  // Block ids live in an LDS window so that gathers never wait on a table read.  A checked run
+  // turns a bad id into -1 (the positions of that block then read as zero and are flagged).
+  const int nblk_kv = (kv_end + kBlockSize - 1) / kBlockSize;
+  int win0 = 0;
+  auto fill_ids = [&](int first) {
+    for (int j = threadIdx.x; j < kIdWindow; j += kPreThreads)
+      ids[j] = first + j < nblk_kv ? load_block_id<CHECK>(table, first + j, num_blocks, err_flag) : -1;
+  };
+
   // Tile pair p holds key tiles 2p and 2p+1; all 512 threads gather it through the block table.
   uint4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_pair = [&](int p) {
+    // Whole pair inside the keys (and unchecked ids): plain loads, nothing to zero.
+    const bool full = !CHECK && (2 * p + 2) * C::KT <= kv_end;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int f = threadIdx.x + kPreThreads * i;
@@ -119,18 +133,38 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       const int rem = f - tt * (C::KT * C::CPR);
       const int row = rem / C::CPR, col = (rem % C::CPR) * 8;
       const int key = (2 * p + tt) * C::KT + row;
-      uint4 kv = uint4{0, 0, 0, 0}, vv = uint4{0, 0, 0, 0};
-      if (key < kv_end) {
-        const int b = load_block_id<CHECK>(table, key / kBlockSize, num_blocks, err_flag);
-        if (b >= 0) {
-          const int64_t o = pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + col;
-          kv = ld16(key_pool + o);
-          vv = ld16(value_pool + o);
+      if (full) {
+        const int64_t o = pool_row_offset(ids[key / kBlockSize - win0], key % kBlockSize, num_kv_heads, g, HD) + col;
+        kreg[i] = ld16(key_pool + o);
+        vreg[i] = ld16(value_pool + o);
+      } else {
+        uint4 kv = uint4{0, 0, 0, 0}, vv = uint4{0, 0, 0, 0};
+        if (key < kv_end) {
+          const int b = ids[key / kBlockSize - win0];
+          if (b >= 0) {
+            const int64_t o = pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + col;
+            kv = ld16(key_pool + o);
+            vv = ld16(value_pool + o);
+          }
         }
+        kreg[i] = kv;
+        vreg[i] = vv;
       }
-      kreg[i] = kv;
-      vreg[i] = vv;
     }
+  };
+  // One 4-byte read per 128-byte line of pair p: pulls the pair into L2 ahead of its gather.
+  auto touch_pair = [&](int p) -> uint32_t {
+    const int line = threadIdx.x;
+    if (line >= 2 * C::LINES) return 0u;
+    const int tensor = line / C::LINES, rem = line - tensor * C::LINES;
+    constexpr int LPRL = HD * 2 / 128;
+    const int key = 2 * p * C::KT + rem / LPRL;
+    if (key >= kv_end || key / kBlockSize - win0 >= kIdWindow) return 0u;
+    const int b = ids[key / kBlockSize - win0];
+    if (b < 0) return 0u;
+    const uint16_t* base = tensor ? value_pool : key_pool;
+    const int64_t o = pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + (rem % LPRL) * 64;
+    return *reinterpret_cast<const volatile uint32_t*>(base + o);
   };
   auto store_pair = [&](int buf) {
 #pragma unroll
@@ -147,15 +181,26 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
 
   const int ntiles = (kv_end + C::KT - 1) / C::KT;
   const int npairs = (ntiles + 1) / 2;
+  fill_ids(0);
+  __syncthreads();
   load_pair(0);
+  uint32_t touched = npairs > 1 ? touch_pair(1) : 0u, touch_sink = 0u;
   store_pair(0);
   __syncthreads();
 
   const int li = lane & 15, dg = (lane >> 4) & 1;
   constexpr int VP = C::VPITCH / 2;
+  constexpr int kPairBlocks = 2 * C::KT / kBlockSize;
   for (int pr = 0; pr < npairs; ++pr) {
     const int cur = pr & 1;
+    // Slide the id window when pair pr + 2 (the furthest one read ahead) leaves it.
+    if ((pr + 3) * kPairBlocks - win0 > kIdWindow && (pr + 1) * kPairBlocks < nblk_kv) {
+      win0 = (pr + 1) * kPairBlocks;
+      fill_ids(win0);
+      __syncthreads();
+    }
     if (pr + 1 < npairs) load_pair(pr + 1);
+    const uint32_t touch_next = pr + 2 < npairs ? touch_pair(pr + 2) : 0u;
     const int kt = 2 * pr + grp;
     const int key0 = kt * C::KT;
     const bool active = kt < ntiles && wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
@@ -164,11 +209,11 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       floatx16 sacc[C::MS];
 #pragma unroll
       for (int ms = 0; ms < C::MS; ++ms) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[ms][e] = 0.f;
         const char* krow = tile + (32 * ms + qc) * C::KPITCH + 16 * hh;
+        sacc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow), qf[0],
+                                                           floatx16{}, 0, 0, 0);
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+        for (int ks = 1; ks < C::KS; ++ks) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
           sacc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[ms], 0, 0, 0);
         }
@@ -204,18 +249,28 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
         for (int md = 0; md < C::MD; ++md) acc[md] *= alpha;
       }
       // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
+      // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
       const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      float psum = 0.f;
-      bf16x8 pb[C::KA];
+      // p = 2^(s * scale * log2e - m_ref), rounded to bf16 pairs: these are both the B operand of the
+      // P.V product and, summed in fp32, the row normaliser (so numerator and denominator use the
+      // same rounded weights).
+      uint32_t pw[C::MS * 8];
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[ms][e], scale_log2, neg_m));
-          psum += p;
-          pb[2 * ms + (e >> 3)][e & 7] = static_cast<__bf16>(p);
+        for (int q = 0; q < 8; ++q) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[ms][2 * q], scale_log2, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[ms][2 * q + 1], scale_log2, neg_m));
+          const uint32_t w = pack_bf16x2(p0, p1);
+          pw[ms * 8 + q] = w;
+          if (q & 1) ps1 = add_bf16x2(w, ps1); else ps0 = add_bf16x2(w, ps0);
         }
-      l_run += psum;
+      l_run += ps0 + ps1;
+      bf16x8 pb[C::KA];
+#pragma unroll
+      for (int a = 0; a < C::KA; ++a)
+        pb[a] = __builtin_bit_cast(bf16x8, uint4{pw[4 * a], pw[4 * a + 1], pw[4 * a + 2], pw[4 * a + 3]});
 
       // O^T += V^T P^T.  k-step a covers keys 16a + 4hh + e and 16a + 8 + 4hh + e (e = 0..3),
       // matching pb[a]; the A operand lane (l % 32 = d, hh) reads those keys' V at d.
@@ -232,8 +287,11 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       }
     }
     if (pr + 1 < npairs) store_pair(cur ^ 1);
+    touch_sink ^= touched;  // issued before this pair's gathers, so already complete
+    touched = touch_next;
     __syncthreads();
   }
+  if (touch_sink == 0x9e3779b9u && threadIdx.x == kPreThreads) m_ref += 1.f;  // keeps the touches alive
 
   // Merge the two key groups: group 1 parks its state in LDS, group 0 combines and writes.
   l_run += __shfl_xor(l_run, 32);

@@ -37,7 +37,8 @@ pkv_status launch_status() { return hipGetLastError() == hipSuccess ? PKV_OK : P
 
 }  // namespace pkv_host
 
-// Streaming-read reference: every byte of the buffer is read once with 16-byte loads and folded
+// Streaming-read reference: every byte of the buffer is read once with non-temporal 16-byte loads
+// (four in flight per thread, two workgroups per CU) and folded
 // into one word per workgroup, which is XOR-ed into *sink.  Used to measure the bandwidth a plain
 // read stream reaches on the device, next to the decode's.
 namespace {
@@ -47,7 +48,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    const uint4 a = pkv::ld16_nt(p + i), b = pkv::ld16_nt(p + i + stride), c = pkv::ld16_nt(p + i + 2 * stride),
+                d = pkv::ld16_nt(p + i + 3 * stride);
     acc ^= a.x ^ a.w ^ b.y ^ b.z ^ c.x ^ c.w ^ d.y ^ d.z;
   }
   for (; i < n16; i += stride) acc ^= p[i].x ^ p[i].w;
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
 extern "C" pkv_status pkv_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) % 16) != 0) return PKV_ERR_INVALID_ARG;
   if (bytes == 0) return PKV_OK;
-  const int blocks = pkv_host::cu_count() * 8;
+  const int blocks = pkv_host::cu_count() * 2;  // the fastest plain read stream measured on MI355X
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(buf), bytes / 16, sink);
   return pkv_host::launch_status();
