@@ -121,50 +121,54 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       ids[j] = first + j < nblk_kv ? load_block_id<CHECK>(table, first + j, num_blocks, err_flag) : -1;
   };
 
-  // Tile pair p holds key tiles 2p and 2p+1; all 512 threads gather it through the block table.
+  // Tile pair p holds key tiles 2p and 2p+1 (2*KT positions); all 512 threads gather it through
+  // the block table.  Thread t's i-th 16-byte chunk is row t / CPR + i * RPI of the pair at column
+  // (t % CPR) * 8; RPI is a multiple of 16, so the row's slot inside its block is the same for
+  // every i and only the block id changes.
+  constexpr int RPI = kPreThreads / C::CPR;  // pair rows per load round
+  const int t_row = threadIdx.x / C::CPR;
+  const int64_t blk_stride = static_cast<int64_t>(kBlockSize) * num_kv_heads * HD;
+  const int64_t c0 = pool_row_offset(0, t_row % kBlockSize, num_kv_heads, g, HD) + (threadIdx.x % C::CPR) * 8;
   uint4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_pair = [&](int p) {
-    // Whole pair inside the keys (and unchecked ids): plain loads, nothing to zero.
-    const bool full = !CHECK && (2 * p + 2) * C::KT <= kv_end;
+    const int key0p = 2 * p * C::KT + t_row;
+    const int idx0 = key0p / kBlockSize - win0;
+    int idv[C::LOADS];
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int f = threadIdx.x + kPreThreads * i;
-      const int tt = f / (C::KT * C::CPR);
-      const int rem = f - tt * (C::KT * C::CPR);
-      const int row = rem / C::CPR, col = (rem % C::CPR) * 8;
-      const int key = (2 * p + tt) * C::KT + row;
-      if (full) {
-        const int64_t o = pool_row_offset(ids[key / kBlockSize - win0], key % kBlockSize, num_kv_heads, g, HD) + col;
+    for (int i = 0; i < C::LOADS; ++i) idv[i] = ids[idx0 + i * (RPI / kBlockSize)];
+    // Whole pair inside the keys (and unchecked ids): plain loads, nothing to mask.
+    if (!CHECK && (2 * p + 2) * C::KT <= kv_end) {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int64_t o = static_cast<int64_t>(idv[i]) * blk_stride + c0;
         kreg[i] = ld16(key_pool + o);
         vreg[i] = ld16(value_pool + o);
-      } else {
-        uint4 kv = uint4{0, 0, 0, 0}, vv = uint4{0, 0, 0, 0};
-        if (key < kv_end) {
-          const int b = ids[key / kBlockSize - win0];
-          if (b >= 0) {
-            const int64_t o = pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + col;
-            kv = ld16(key_pool + o);
-            vv = ld16(value_pool + o);
-          }
-        }
-        kreg[i] = kv;
-        vreg[i] = vv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const bool ok = key0p + i * RPI < kv_end && idv[i] >= 0;
+        const int64_t o = static_cast<int64_t>(ok ? idv[i] : 0) * blk_stride + c0;  // block 0 stands in
+        const uint4 kv = ld16(key_pool + o), vv = ld16(value_pool + o);
+        kreg[i] = ok ? kv : uint4{0, 0, 0, 0};
+        vreg[i] = ok ? vv : uint4{0, 0, 0, 0};
       }
     }
   };
-  // One 4-byte read per 128-byte line of pair p: pulls the pair into L2 ahead of its gather.
+  // One 4-byte read per 128-byte line of pair p: pulls the pair into L2 ahead of its gather.  The
+  // value is folded into a sink one pair later, so nothing waits on it.
+  constexpr int LPRL = HD * 2 / 128;  // lines per row
   auto touch_pair = [&](int p) -> uint32_t {
     const int line = threadIdx.x;
     if (line >= 2 * C::LINES) return 0u;
     const int tensor = line / C::LINES, rem = line - tensor * C::LINES;
-    constexpr int LPRL = HD * 2 / 128;
     const int key = 2 * p * C::KT + rem / LPRL;
-    if (key >= kv_end || key / kBlockSize - win0 >= kIdWindow) return 0u;
+    if (key >= kv_end) return 0u;
     const int b = ids[key / kBlockSize - win0];
     if (b < 0) return 0u;
     const uint16_t* base = tensor ? value_pool : key_pool;
-    const int64_t o = pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + (rem % LPRL) * 64;
-    return *reinterpret_cast<const volatile uint32_t*>(base + o);
+    return *reinterpret_cast<const uint32_t*>(
+        base + pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + (rem % LPRL) * 64);
   };
   auto store_pair = [&](int buf) {
 #pragma unroll
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     touched = touch_next;
     __syncthreads();
   }
-  if (touch_sink == 0x9e3779b9u && threadIdx.x == kPreThreads) m_ref += 1.f;  // keeps the touches alive
+  if (touch_sink == 0x9e3779b9u && causal == 0x5eed) m_ref += 1.f;  // keeps the touches alive
 
   // Merge the two key groups: group 1 parks its state in LDS, group 0 combines and writes.
   l_run += __shfl_xor(l_run, 32);
@@ -361,6 +365,7 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
   if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (num_blocks == 0) return PKV_ERR_INVALID_ARG;  // a non-empty chunk needs cached positions
   if (!out || !query || !cu_q_lens || !chunk_offsets || !key_pool || !value_pool || !block_tables)
     return PKV_ERR_INVALID_ARG;
   const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
