@@ -108,7 +108,7 @@ pkv_status pkv_cache_write(const void* key, const void* value, int64_t key_tok_s
                            pkv_dtype dtype, int32_t* err_flag, void* stream);
 
 /*
- * Paged gather ([C13-L2] figure 按块表取 K: K_r = gather(K_pool, table_r), values alike).
+ * Paged gather ([C13-L2] figure 按块表取 K: a request's K is the pool rows named by its table, V alike).
  * Copies sequence s's first lengths[s] token rows of both pools, in logical order, into
  * key_out / value_out rows cu_out[s] .. cu_out[s] + lengths[s] - 1, bit for bit, using the same
  * address arithmetic as the attention kernels.  A diagnostic used to test block indexing.
