@@ -30,6 +30,18 @@ __device__ __forceinline__ int64_t pool_row_offset(int block, int offset, int nu
          static_cast<int64_t>(head_dim);
 }
 
+// Byte offset of (block, in-block offset c_bytes) in a pool whose blocks are blk_bytes long.  With
+// NARROW (the whole pool below 4 GiB and fewer than 2^24 blocks) the offset is a 32-bit value built
+// with a 24-bit multiply, which lets the load use a scalar base plus a 32-bit vector offset.
+template <bool NARROW>
+__device__ __forceinline__ const char* pool_at(const void* pool, int block, uint32_t blk_bytes, uint32_t c_bytes) {
+  if constexpr (NARROW) {
+    return static_cast<const char*>(pool) + (__umul24(static_cast<uint32_t>(block), blk_bytes) + c_bytes);
+  } else {
+    return static_cast<const char*>(pool) + (static_cast<int64_t>(block) * blk_bytes + c_bytes);
+  }
+}
+
 // Reads the physical block of logical block `j` of a sequence.  In checked mode an id outside
 // [0, num_blocks) sets PKV_FLAG_BAD_BLOCK and yields -1 so the caller skips the page.
 template <bool CHECK>

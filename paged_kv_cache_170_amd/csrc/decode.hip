@@ -121,10 +121,39 @@ struct DecBuf {
 
 // One work item: positions [split * split_tokens, min(+split_tokens, ctx)) of sequence s, KV head g,
 // for all query heads of the group.  Called by all 256 threads of the workgroup.
+// What a work item needs before its first gather: where it is, its block ids (one per lane) and the
+// query fragment.  Loaded one item ahead so that these reads overlap the previous item's work.
+template <int HD>
+struct DecItem {
+  int s, g, split, ctx, nsplit;
+  int my_id;
+  bf16x8 qf[DecCfg<HD>::KK];
+};
+
 template <int HD, bool CHECK>
-__device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g, int split, int ctx, int nsplit,
-                                                 char* smem) {
+__device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<HD>& it) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = lane & 15, c = lane >> 4;
+  const int tok0 = it.split * A_.split_tokens;
+  const int tok_end = min(tok0 + A_.split_tokens, it.ctx);
+  const int32_t* table = A_.block_tables + static_cast<int64_t>(it.s) * A_.max_blocks;
+  // The split's block ids, one per lane (a split spans at most 64 blocks).
+  const int nblk_split = it.ctx > 0 ? (tok_end - tok0 + kBlockSize - 1) / kBlockSize : 0;
+  it.my_id = lane < nblk_split ? load_block_id<CHECK>(table, tok0 / kBlockSize + lane, A_.num_blocks, A_.err_flag) : -1;
+  // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.
+  const bool live = n < A_.group && it.ctx > 0;
+  const uint16_t* qrow =
+      A_.query + (static_cast<int64_t>(it.s) * A_.num_q_heads + it.g * A_.group + (live ? n : 0)) * HD + 8 * c;
+#pragma unroll
+  for (int kk = 0; kk < DecCfg<HD>::KK; ++kk) it.qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
+}
+
+template <int HD, bool CHECK, bool NARROW>
+__device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecItem<HD>& it, char* smem) {
   using C = DecCfg<HD>;
+  const int s = it.s, g = it.g, split = it.split, ctx = it.ctx, nsplit = it.nsplit;
+  const int my_id = it.my_id;
+  const bf16x8* qf = it.qf;
   const uint16_t* __restrict__ key_pool = A_.key_pool;
   const uint16_t* __restrict__ value_pool = A_.value_pool;
   const int num_q_heads = A_.num_q_heads, num_kv_heads = A_.num_kv_heads, group = A_.group;
@@ -136,21 +165,6 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
   const int n = lane & 15, c = lane >> 4;
   const int tok0 = split * split_tokens;
   const int tok_end = min(tok0 + split_tokens, ctx);
-  const int32_t* table = A_.block_tables + static_cast<int64_t>(s) * A_.max_blocks;
-
-  // The split's block ids, one per lane (a split spans at most 64 blocks).
-  const int nblk_split = (tok_end - tok0 + kBlockSize - 1) / kBlockSize;
-  const int my_id = lane < nblk_split ? load_block_id<CHECK>(table, tok0 / kBlockSize + lane, num_blocks, err_flag) : -1;
-
-  // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.
-  bf16x8 qf[C::KK];
-  {
-    const bool live = n < group;
-    const uint16_t* qrow =
-        A_.query + (static_cast<int64_t>(s) * num_q_heads + g * group + (live ? n : 0)) * HD + 8 * c;
-#pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
-  }
 
   float m_ref = -INFINITY, l_run = 0.f;
   floatx4 acc[C::MT];
@@ -164,6 +178,9 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
 
   // Step u covers positions tok0 + 32u .. +31 (two blocks).  K and V rows are read whole (each
   // wave-wide load covers RPL complete rows) and staged in LDS in their natural layout.
+  const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * 2);
+  const uint32_t row_bytes = static_cast<uint32_t>(num_kv_heads * HD * 2);
+  const uint32_t c0 = static_cast<uint32_t>((row_base * num_kv_heads + g) * HD * 2 + col * 2);
   auto load = [&](int u, DecBuf<HD>& B) {
     const int t0 = tok0 + 32 * u;
     B.b0 = __builtin_amdgcn_readlane(my_id, 2 * u);
@@ -174,9 +191,9 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
 #pragma unroll
       for (int i = 0; i < C::VLD; ++i) {
         if (b >= 0) {
-          const int64_t o = pool_row_offset(b, i * C::RPL + row_base, num_kv_heads, g, HD) + col;
-          B.k[pg][i] = ld16(key_pool + o);
-          B.v[pg][i] = ld16(value_pool + o);
+          const uint32_t cb = c0 + static_cast<uint32_t>(i * C::RPL) * row_bytes;
+          B.k[pg][i] = ld16(pool_at<NARROW>(key_pool, b, blk_bytes, cb));
+          B.v[pg][i] = ld16(pool_at<NARROW>(value_pool, b, blk_bytes, cb));
         } else {
           B.k[pg][i] = uint4{0, 0, 0, 0};
           B.v[pg][i] = uint4{0, 0, 0, 0};
@@ -290,7 +307,7 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, int s, int g
 // the lengths and no workgroup is launched without work.  With gridDim.x a multiple of 8 and
 // Hkv = 8, KV head g always lands on the same XCD (workgroups are dealt round-robin over the 8
 // XCDs), so blocks shared between sequences stay in that XCD's L2.
-template <int HD, bool CHECK>
+template <int HD, bool CHECK, bool NARROW>
 __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, int num_seqs) {
   __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
   __shared__ int pref[kDecThreads];
@@ -298,6 +315,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, int
   const int stride = gridDim.x;
   int next = blockIdx.x;
   int base = 0;
+  DecItem<HD> cur, nxt;
   for (int c0 = 0; c0 < num_seqs; c0 += kDecThreads) {
     const int sq = c0 + tid;
     int cnt = 0;
@@ -316,26 +334,41 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, int
       __syncthreads();
     }
     const int chunk_total = pref[kDecThreads - 1];
-    while (next < base + chunk_total) {
-      const int local = next - base;
-      int lo = 0, hi = kDecThreads - 1;  // first j with pref[j] > local
+    // Item k of this chunk: sequence c0 + j for the first j with pref[j] > k.
+    auto find = [&](int item, DecItem<HD>& it) {
+      const int local = item - base;
+      int lo = 0, hi = kDecThreads - 1;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (pref[mid] > local) hi = mid; else lo = mid + 1;
       }
-      const int s = c0 + lo;
+      it.s = c0 + lo;
       const int r = local - (lo ? pref[lo - 1] : 0);
-      const int split = r / a.num_kv_heads, g = r - split * a.num_kv_heads;
-      const int ctx = clamp_ctx<CHECK>(a.context_lens[s], a.max_blocks, a.err_flag, false);
-      if (ctx == 0) {
+      it.split = r / a.num_kv_heads;
+      it.g = r - it.split * a.num_kv_heads;
+      it.ctx = clamp_ctx<CHECK>(a.context_lens[it.s], a.max_blocks, a.err_flag, false);
+      it.nsplit = (it.ctx + a.split_tokens - 1) / a.split_tokens;
+    };
+    if (next < base + chunk_total) {
+      find(next, cur);
+      decode_item_prologue<HD, CHECK>(a, cur);
+    }
+    while (next < base + chunk_total) {
+      const int nn = next + stride;
+      const bool have_next = nn < base + chunk_total;
+      if (have_next) {
+        find(nn, nxt);
+        decode_item_prologue<HD, CHECK>(a, nxt);  // in flight while this item runs
+      }
+      if (cur.ctx == 0) {
         for (int i = tid; i < a.group * HD; i += kDecThreads)
-          store_out(a.out, (static_cast<int64_t>(s) * a.num_q_heads + g * a.group) * HD + i, 0.f, a.out_bf16);
+          store_out(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + cur.g * a.group) * HD + i, 0.f, a.out_bf16);
       } else {
-        const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-        decode_bf16_item<HD, CHECK>(a, s, g, split, ctx, nsplit, smem);
+        decode_bf16_item<HD, CHECK, NARROW>(a, cur, smem);
       }
       __syncthreads();  // the next item reuses the staging and merge areas
-      next += stride;
+      next = nn;
+      if (have_next) cur = nxt;
     }
     base += chunk_total;
   }
@@ -484,15 +517,32 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   for (int i = threadIdx.x; i < group * head_dim; i += blockDim.x) {
     const int h = g * group + i / head_dim, d = i % head_dim;
     const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_splits;
-    float M = -INFINITY;
-    for (int p = 0; p < nsplit; ++p) M = fmaxf(M, ws_ml[(base + p) * 2]);
-    float O = 0.f, L = 0.f;
-#pragma unroll 4
-    for (int p = 0; p < nsplit; ++p) {
-      const float mp = ws_ml[(base + p) * 2];
-      const float f = (mp == -INFINITY) ? 0.f : fast_exp2(mp - M);
-      O += f * ws_o[(base + p) * head_dim + d];
-      L += f * ws_ml[(base + p) * 2 + 1];
+    // One pass with a running max; the loads of a batch of splits are independent and issue together.
+    float M = -INFINITY, O = 0.f, L = 0.f;
+    for (int p0 = 0; p0 < nsplit; p0 += 8) {
+      float mp[8], lp[8], op[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool live = p0 + k < nsplit;
+        const int64_t part = base + (live ? p0 + k : p0);
+        mp[k] = live ? ws_ml[part * 2] : -INFINITY;
+        lp[k] = ws_ml[part * 2 + 1];
+        op[k] = ws_o[part * head_dim + d];
+      }
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mp[k]);
+      if (Mn == -INFINITY) continue;
+      const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+      O *= a;
+      L *= a;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = (mp[k] == -INFINITY) ? 0.f : fast_exp2(mp[k] - Mn);
+        O += f * op[k];
+        L += f * lp[k];
+      }
+      M = Mn;
     }
     store_out(out, (static_cast<int64_t>(s) * num_q_heads + h) * head_dim + d, L > 0.f ? O / L : 0.f, out_bf16 != 0);
   }
@@ -609,13 +659,21 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
     const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * max_splits;
     const int64_t resident = static_cast<int64_t>(pkv_host::cu_count()) * (head_dim <= 128 ? 2 : 1);
     const dim3 pgrid(static_cast<unsigned>(max_items < resident ? max_items : resident));
-#define PKV_DEC_BF16(HD, CHECK) \
-  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK>), pgrid, dim3(kDecThreads), 0, st, a, num_seqs)
+    const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
+                        num_blocks < (1 << 24);
+#define PKV_DEC_BF16(HD, CHECK, NARROW) \
+  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW>), pgrid, dim3(kDecThreads), 0, st, a, num_seqs)
+#define PKV_DEC_BF16_N(HD, CHECK) \
+  if (narrow) PKV_DEC_BF16(HD, CHECK, true); else PKV_DEC_BF16(HD, CHECK, false);
+#define PKV_DEC_BF16_C(HD) \
+  if (err_flag) { PKV_DEC_BF16_N(HD, true) } else { PKV_DEC_BF16_N(HD, false) }
     switch (head_dim) {
-      case 64: if (err_flag) PKV_DEC_BF16(64, true); else PKV_DEC_BF16(64, false); break;
-      case 128: if (err_flag) PKV_DEC_BF16(128, true); else PKV_DEC_BF16(128, false); break;
-      default: if (err_flag) PKV_DEC_BF16(256, true); else PKV_DEC_BF16(256, false); break;
+      case 64: PKV_DEC_BF16_C(64) break;
+      case 128: PKV_DEC_BF16_C(128) break;
+      default: PKV_DEC_BF16_C(256) break;
     }
+#undef PKV_DEC_BF16_C
+#undef PKV_DEC_BF16_N
 #undef PKV_DEC_BF16
   } else {
     if (err_flag) { PKV_DEC_HD(decode_f32_kernel, float, true) } else { PKV_DEC_HD(decode_f32_kernel, float, false) }

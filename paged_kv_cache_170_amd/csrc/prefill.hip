@@ -55,7 +55,7 @@ struct PreCfg {
   static_assert(LOADS * kPreThreads == 2 * KT * CPR, "pair loads must divide evenly");
 };
 
-template <int HD, bool CHECK>
+template <int HD, bool CHECK, bool NARROW>
 __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     const uint16_t* __restrict__ query, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ chunk_offsets, const uint16_t* __restrict__ key_pool,
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
   // every i and only the block id changes.
   constexpr int RPI = kPreThreads / C::CPR;  // pair rows per load round
   const int t_row = threadIdx.x / C::CPR;
-  const int64_t blk_stride = static_cast<int64_t>(kBlockSize) * num_kv_heads * HD;
-  const int64_t c0 = pool_row_offset(0, t_row % kBlockSize, num_kv_heads, g, HD) + (threadIdx.x % C::CPR) * 8;
+  const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * 2);
+  const uint32_t c0 = static_cast<uint32_t>(((t_row % kBlockSize) * num_kv_heads + g) * HD * 2 + (threadIdx.x % C::CPR) * 16);
   uint4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_pair = [&](int p) {
     const int key0p = 2 * p * C::KT + t_row;
@@ -140,16 +140,16 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     if (!CHECK && (2 * p + 2) * C::KT <= kv_end) {
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
-        const int64_t o = static_cast<int64_t>(idv[i]) * blk_stride + c0;
-        kreg[i] = ld16(key_pool + o);
-        vreg[i] = ld16(value_pool + o);
+        kreg[i] = ld16(pool_at<NARROW>(key_pool, idv[i], blk_bytes, c0));
+        vreg[i] = ld16(pool_at<NARROW>(value_pool, idv[i], blk_bytes, c0));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
         const bool ok = key0p + i * RPI < kv_end && idv[i] >= 0;
-        const int64_t o = static_cast<int64_t>(ok ? idv[i] : 0) * blk_stride + c0;  // block 0 stands in
-        const uint4 kv = ld16(key_pool + o), vv = ld16(value_pool + o);
+        const int b = ok ? idv[i] : 0;  // block 0 stands in for masked rows
+        const uint4 kv = ld16(pool_at<NARROW>(key_pool, b, blk_bytes, c0));
+        const uint4 vv = ld16(pool_at<NARROW>(value_pool, b, blk_bytes, c0));
         kreg[i] = ok ? kv : uint4{0, 0, 0, 0};
         vreg[i] = ok ? vv : uint4{0, 0, 0, 0};
       }
@@ -167,8 +167,8 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     const int b = ids[key / kBlockSize - win0];
     if (b < 0) return 0u;
     const uint16_t* base = tensor ? value_pool : key_pool;
-    return *reinterpret_cast<const uint32_t*>(
-        base + pool_row_offset(b, key % kBlockSize, num_kv_heads, g, HD) + (rem % LPRL) * 64);
+    const uint32_t cb = static_cast<uint32_t>(((key % kBlockSize) * num_kv_heads + g) * HD * 2 + (rem % LPRL) * 128);
+    return *reinterpret_cast<const uint32_t*>(pool_at<NARROW>(base, b, blk_bytes, cb));
   };
   auto store_pair = [&](int buf) {
 #pragma unroll
@@ -375,21 +375,25 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
   const float scale_log2 = scale * kLog2e;
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
-#define PKV_PRE(HD, CHECK)                                                                                      \
-  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK>), dim3(static_cast<unsigned>(items)), dim3(kPreThreads),    \
-                     0,                                                                                         \
-                     st, static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets,                         \
+  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
+                      num_blocks < (1 << 24);
+#define PKV_PRE(HD, CHECK, NARROW)                                                                                \
+  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK, NARROW>), dim3(static_cast<unsigned>(items)),               \
+                     dim3(kPreThreads), 0, st, static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets,    \
                      static_cast<const uint16_t*>(key_pool), static_cast<const uint16_t*>(value_pool),           \
                      block_tables, max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks,    \
                      causal != 0, scale_log2, out, ob, err_flag)
-#define PKV_PRE_HD(CHECK)                       \
-  switch (head_dim) {                           \
-    case 64: PKV_PRE(64, CHECK); break;         \
-    case 128: PKV_PRE(128, CHECK); break;       \
-    default: PKV_PRE(256, CHECK); break;        \
+#define PKV_PRE_N(HD, CHECK) \
+  if (narrow) PKV_PRE(HD, CHECK, true); else PKV_PRE(HD, CHECK, false);
+#define PKV_PRE_HD(CHECK)                         \
+  switch (head_dim) {                             \
+    case 64: PKV_PRE_N(64, CHECK) break;          \
+    case 128: PKV_PRE_N(128, CHECK) break;        \
+    default: PKV_PRE_N(256, CHECK) break;         \
   }
   if (err_flag) { PKV_PRE_HD(true) } else { PKV_PRE_HD(false) }
 #undef PKV_PRE_HD
+#undef PKV_PRE_N
 #undef PKV_PRE
   return pkv_host::launch_status();
 }
