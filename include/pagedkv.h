@@ -149,7 +149,7 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   query               [num_seqs, num_q_heads, head_dim], dtype `dtype` (the pool dtype)
  *   context_lens        int32 [num_seqs] (device), each <= max_blocks_per_seq * 16
  *   scale               > 0 (the usual 1/sqrt(head_dim)); other values are PKV_ERR_INVALID_ARG
- *   split_tokens        0 for the default, else a multiple of 128 in [128, 1024]
+ *   split_tokens        0 for the default, else a multiple of 128 in [128, 2048]
  *   workspace           device scratch of >= pkv_decode_workspace_bytes(...) bytes; contents on
  *                       entry are ignored; must not be shared by calls running concurrently.
  */

@@ -126,7 +126,7 @@ struct DecBuf {
 template <int HD>
 struct DecItem {
   int s, g, split, ctx, nsplit;
-  int my_id;
+  int my_id[2];  // block ids of the split: lane j holds blocks j and 64 + j
   bf16x8 qf[DecCfg<HD>::KK];
 };
 
@@ -137,9 +137,12 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   const int tok0 = it.split * A_.split_tokens;
   const int tok_end = min(tok0 + A_.split_tokens, it.ctx);
   const int32_t* table = A_.block_tables + static_cast<int64_t>(it.s) * A_.max_blocks;
-  // The split's block ids, one per lane (a split spans at most 64 blocks).
+  // The split's block ids, two per lane (a split spans at most 128 blocks).
   const int nblk_split = it.ctx > 0 ? (tok_end - tok0 + kBlockSize - 1) / kBlockSize : 0;
-  it.my_id = lane < nblk_split ? load_block_id<CHECK>(table, tok0 / kBlockSize + lane, A_.num_blocks, A_.err_flag) : -1;
+  const int j0 = tok0 / kBlockSize;
+  it.my_id[0] = lane < nblk_split ? load_block_id<CHECK>(table, j0 + lane, A_.num_blocks, A_.err_flag) : -1;
+  it.my_id[1] = lane + kWave < nblk_split ? load_block_id<CHECK>(table, j0 + kWave + lane, A_.num_blocks, A_.err_flag)
+                                          : -1;
   // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.
   const bool live = n < A_.group && it.ctx > 0;
   const uint16_t* qrow =
@@ -152,7 +155,7 @@ template <int HD, bool CHECK, bool NARROW>
 __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecItem<HD>& it, char* smem) {
   using C = DecCfg<HD>;
   const int s = it.s, g = it.g, split = it.split, ctx = it.ctx, nsplit = it.nsplit;
-  const int my_id = it.my_id;
+  const int my_id0 = it.my_id[0], my_id1 = it.my_id[1];
   const bf16x8* qf = it.qf;
   const uint16_t* __restrict__ key_pool = A_.key_pool;
   const uint16_t* __restrict__ value_pool = A_.value_pool;
@@ -183,8 +186,11 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   const uint32_t c0 = static_cast<uint32_t>((row_base * num_kv_heads + g) * HD * 2 + col * 2);
   auto load = [&](int u, DecBuf<HD>& B) {
     const int t0 = tok0 + 32 * u;
-    B.b0 = __builtin_amdgcn_readlane(my_id, 2 * u);
-    B.b1 = (t0 + kBlockSize < ctx) ? __builtin_amdgcn_readlane(my_id, 2 * u + 1) : -1;
+    // Blocks 2u and 2u + 1 of the split (u is the same across the wave).
+    const int idreg = u < kWave / 2 ? my_id0 : my_id1;
+    const int lane_b = (2 * u) & (kWave - 1);
+    B.b0 = __builtin_amdgcn_readlane(idreg, lane_b);
+    B.b1 = (t0 + kBlockSize < ctx) ? __builtin_amdgcn_readlane(idreg, lane_b + 1) : -1;
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       const int b = pg ? B.b1 : B.b0;
@@ -559,7 +565,7 @@ int env_split_tokens() {
     const char* e = std::getenv("PKV_SPLIT_TOKENS");
     if (!e) return 0;
     const int x = std::atoi(e);
-    return (x > 0 && x % 128 == 0 && x <= 1024) ? x : 0;
+    return (x > 0 && x % 128 == 0 && x <= 2048) ? x : 0;
   }();
   return v;
 }
@@ -590,7 +596,7 @@ extern "C" int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads
   const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
   // Prefer long splits (fewer partials, fewer merges) while the largest possible number of work
   // items still fills two workgroups per CU.
-  for (int S : {1024, 512, 256})
+  for (int S : {2048, 1024, 512, 256})
     if (pairs * ((max_ctx + S - 1) / S) >= 512) return S;
   return 128;
 }
@@ -598,7 +604,7 @@ extern "C" int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq, int32_t split_tokens) {
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 0;
-  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 1024) return 0;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 2048) return 0;
   const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
   const int64_t max_splits = (static_cast<int64_t>(max_blocks_per_seq) * kBlockSize + S - 1) / S;
   if (max_splits <= 1) return 0;
@@ -614,7 +620,7 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
                                             int32_t* err_flag, void* stream) {
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
     return PKV_ERR_INVALID_ARG;
-  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 1024) return PKV_ERR_INVALID_ARG;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 2048) return PKV_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return PKV_ERR_UNSUPPORTED;

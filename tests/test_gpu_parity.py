@@ -242,12 +242,12 @@ def test_long_decode_full(pkv, dev):
 
 
 def test_decode_split_size_invariance_and_determinism(pkv, dev):
-    _say("case gqa_decode subset: split sizes 128..1024, repeated runs")
+    _say("case decode subset: split sizes 128..2048, repeated runs")
     c = wl.random_case(91, kind="decode", dtype="bf16", num_seqs=9, num_q_heads=16, num_kv_heads=2, head_dim=128,
                        max_ctx=2100, min_ctx=1, new_tokens=False, poison=True)
     d = Dev(c, dev)
     err = new_err(dev)
-    outs = {s: _decode(pkv, d, err_flag=err, split_tokens=s).cpu().numpy() for s in (128, 256, 512, 1024)}
+    outs = {s: _decode(pkv, d, err_flag=err, split_tokens=s).cpu().numpy() for s in (128, 256, 512, 1024, 2048)}
     ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
     base = outs[512]
     for s, o in outs.items():
