@@ -40,6 +40,9 @@
  *     touching memory out of range; the affected output is then unspecified.  With err_flag ==
  *     NULL the checks are skipped and out-of-range ids are undefined behaviour.
  *   - Empty work (num_tokens == 0, num_seqs == 0) is a successful no-op.
+ *   - The attention calls read and write whole 16-byte vectors: query, out, the pools and the
+ *     decode workspace must be 16-byte aligned, else PKV_ERR_INVALID_ARG.  (The cache write
+ *     accepts any element-aligned pointer and picks its vector width from the alignment.)
  *   - Supported: head_dim in {64, 128, 256}; num_q_heads % num_kv_heads == 0 and
  *     num_q_heads / num_kv_heads <= 16; block_size == 16.  Cache write and decode take fp32 or
  *     bf16; the prefill chunk takes bf16 (bf16 MFMA with fp32 accumulation).  Outputs may be
@@ -131,8 +134,9 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 /*
  * Workspace bytes pkv_paged_attn_decode needs for these shapes and split size (0 = the default
- * above): per (sequence, query head, split) an fp32 partial output row plus its running max and
- * normaliser.  Returns 0 for invalid shapes.
+ * above): the work plan (a 256-byte header and one 4-byte entry per (sequence, split) piece), and,
+ * when a sequence can span several splits, per (sequence, query head, split) an fp32 partial
+ * output row plus its running max and normaliser.  Never 0 for valid shapes; 0 for invalid ones.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_blocks_per_seq, int32_t split_tokens);
@@ -150,8 +154,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   context_lens        int32 [num_seqs] (device), each <= max_blocks_per_seq * 16
  *   scale               > 0 (the usual 1/sqrt(head_dim)); other values are PKV_ERR_INVALID_ARG
  *   split_tokens        0 for the default, else a multiple of 128 in [128, 2048]
- *   workspace           device scratch of >= pkv_decode_workspace_bytes(...) bytes; contents on
- *                       entry are ignored; must not be shared by calls running concurrently.
+ *   workspace           device scratch of >= pkv_decode_workspace_bytes(...) bytes (never null);
+ *                       contents on entry are ignored; must not be shared by calls running
+ *                       concurrently.  bf16 pools: a one-workgroup pass first sorts the pieces
+ *                       longest first into it, and the attention workgroups then take items from
+ *                       that list through counters the pass clears.
  */
 pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
                                  const void* value_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -198,8 +198,8 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
       for (int i = 0; i < C::VLD; ++i) {
         if (b >= 0) {
           const uint32_t cb = c0 + static_cast<uint32_t>(i * C::RPL) * row_bytes;
-          B.k[pg][i] = ld16(pool_at<NARROW>(key_pool, b, blk_bytes, cb));
-          B.v[pg][i] = ld16(pool_at<NARROW>(value_pool, b, blk_bytes, cb));
+          B.k[pg][i] = ld16_nt(pool_at<NARROW>(key_pool, b, blk_bytes, cb));
+          B.v[pg][i] = ld16_nt(pool_at<NARROW>(value_pool, b, blk_bytes, cb));
         } else {
           B.k[pg][i] = uint4{0, 0, 0, 0};
           B.v[pg][i] = uint4{0, 0, 0, 0};
@@ -306,77 +306,118 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
                   A_.out_bf16);
 }
 
-// Persistent form: a fixed grid walks the compact list of work items.  Items are numbered in
-// order of (sequence, split, KV head), each sequence contributing max(1, ceil(ctx / split)) x Hkv of
-// them; workgroup b takes items b, b + gridDim.x, ...  Every workgroup rebuilds the numbering from
-// context_lens with a block-wide prefix sum over 256 sequences at a time, so the host never needs
-// the lengths and no workgroup is launched without work.  With gridDim.x a multiple of 8 and
-// Hkv = 8, KV head g always lands on the same XCD (workgroups are dealt round-robin over the 8
-// XCDs), so blocks shared between sequences stay in that XCD's L2.
-template <int HD, bool CHECK, bool NARROW>
-__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, int num_seqs) {
-  __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
-  __shared__ int pref[kDecThreads];
-  const int tid = threadIdx.x;
-  const int stride = gridDim.x;
-  int next = blockIdx.x;
-  int base = 0;
-  DecItem<HD> cur, nxt;
-  for (int c0 = 0; c0 < num_seqs; c0 += kDecThreads) {
-    const int sq = c0 + tid;
-    int cnt = 0;
-    if (sq < num_seqs) {
-      const int ctx = clamp_ctx<CHECK>(a.context_lens[sq], a.max_blocks, a.err_flag, blockIdx.x == 0);
-      cnt = (ctx == 0 ? 1 : (ctx + a.split_tokens - 1) / a.split_tokens) * a.num_kv_heads;
-    }
-    __syncthreads();  // the previous chunk's searches are done with pref
-    pref[tid] = cnt;
-    __syncthreads();
+// Work plan of the persistent decode.  A piece is one (sequence, split) pair; its length in
+// 32-token steps is at most split_tokens / 32.  One workgroup sorts the pieces longest first (a
+// counting sort on that length: full splits first, then the sequences' last splits by length; an
+// empty sequence counts as one step) into `pieces` as {sequence << 16 | split, context length},
+// stores their number in the plan header and sets the fetch counters.  Longest-first order with
+// dynamic fetching keeps the workgroups' finishing times within about one short piece.
+//
+// Items: item i is piece i / Hkv for KV head i % Hkv.  Workgroup b of the persistent grid draws
+// from queue q = b % queues the items q, q + queues, q + 2 queues, ...; its first two are items b
+// and b + grid (no fetch), the rest come from queue q's counter, which the plan starts at
+// 2 * grid / queues.  Each counter sits on its own 128-byte line.
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxQueues = 64;
+constexpr int kCounterStride = 32;  // ints: one 128-byte line per counter
+constexpr int kPlanTotal = kMaxQueues * kCounterStride;
+constexpr int kPlanInts = kPlanTotal + kCounterStride;
+constexpr int kMaxClasses = 2048 / 32 + 1;
+
+template <bool CHECK>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ context_lens,
+                                                                   int num_seqs, int max_blocks, int split_tokens,
+                                                                   int2* __restrict__ pieces,
+                                                                   int32_t* __restrict__ plan, int grid, int queues,
+                                                                   int32_t* err_flag) {
+  __shared__ int count[kMaxClasses];
+  __shared__ int cursor[kMaxClasses];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int top = split_tokens / 32;  // class of a full split (<= 64)
+  if (tid < kMaxClasses) count[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kPlanThreads) {
+    const int ctx = clamp_ctx<CHECK>(context_lens[s], max_blocks, err_flag, true);
+    const int full = ctx / split_tokens, rem = ctx - full * split_tokens;
+    if (full) atomicAdd(&count[top], full);
+    if (rem || !ctx) atomicAdd(&count[rem ? (rem + 31) / 32 : 1], 1);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // Classes top, top - 1, ..., 1 on lanes 0, 1, ...: exclusive prefix sum over the wave.
+    const int c = top - lane;
+    const int n = c >= 1 ? count[c] : 0;
+    int incl = n;
 #pragma unroll
-    for (int off = 1; off < kDecThreads; off <<= 1) {
-      const int v = tid >= off ? pref[tid - off] : 0;
-      __syncthreads();
-      pref[tid] += v;
-      __syncthreads();
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
     }
-    const int chunk_total = pref[kDecThreads - 1];
-    // Item k of this chunk: sequence c0 + j for the first j with pref[j] > k.
-    auto find = [&](int item, DecItem<HD>& it) {
-      const int local = item - base;
-      int lo = 0, hi = kDecThreads - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (pref[mid] > local) hi = mid; else lo = mid + 1;
-      }
-      it.s = c0 + lo;
-      const int r = local - (lo ? pref[lo - 1] : 0);
-      it.split = r / a.num_kv_heads;
-      it.g = r - it.split * a.num_kv_heads;
-      it.ctx = clamp_ctx<CHECK>(a.context_lens[it.s], a.max_blocks, a.err_flag, false);
-      it.nsplit = (it.ctx + a.split_tokens - 1) / a.split_tokens;
-    };
-    if (next < base + chunk_total) {
-      find(next, cur);
-      decode_item_prologue<HD, CHECK>(a, cur);
+    if (c >= 1) cursor[c] = incl - n;
+    if (lane == kWave - 1) plan[kPlanTotal] = incl;
+  }
+  if (tid < queues) plan[tid * kCounterStride] = 2 * (grid / queues);
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kPlanThreads) {
+    const int ctx = clamp_ctx<false>(context_lens[s], max_blocks, nullptr, false);
+    const int full = ctx / split_tokens, rem = ctx - full * split_tokens;
+    const int tag = static_cast<int>(static_cast<uint32_t>(s) << 16);
+    if (full) {
+      const int at = atomicAdd(&cursor[top], full);
+      for (int k = 0; k < full; ++k) pieces[at + k] = int2{tag | k, ctx};
     }
-    while (next < base + chunk_total) {
-      const int nn = next + stride;
-      const bool have_next = nn < base + chunk_total;
-      if (have_next) {
-        find(nn, nxt);
-        decode_item_prologue<HD, CHECK>(a, nxt);  // in flight while this item runs
-      }
-      if (cur.ctx == 0) {
-        for (int i = tid; i < a.group * HD; i += kDecThreads)
-          store_out(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + cur.g * a.group) * HD + i, 0.f, a.out_bf16);
-      } else {
-        decode_bf16_item<HD, CHECK, NARROW>(a, cur, smem);
-      }
-      __syncthreads();  // the next item reuses the staging and merge areas
-      next = nn;
-      if (have_next) cur = nxt;
+    if (rem || !ctx) pieces[atomicAdd(&cursor[rem ? (rem + 31) / 32 : 1], 1)] = int2{tag | full, ctx};
+  }
+}
+
+// Persistent form: a fixed grid takes work items from the plan (see above).  With queues a
+// multiple of 8 and workgroups dealt round-robin over the 8 XCDs, queue q runs on XCD q % 8 and
+// holds only items with i % 8 == q % 8, so with Hkv = 8 each KV head stays on one XCD and blocks
+// shared between sequences stay in that XCD's L2.  The item after next is fetched while the
+// current item runs; the next item's block ids and query are loaded then too.
+template <int HD, bool CHECK, bool NARROW>
+__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, const int2* __restrict__ pieces,
+                                                                  int32_t* __restrict__ plan, int queues) {
+  __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
+  __shared__ int fetched[2];
+  const int tid = threadIdx.x;
+  const int queue = blockIdx.x % queues;
+  const int total = plan[kPlanTotal] * a.num_kv_heads;
+  auto find = [&](int item, DecItem<HD>& it) {
+    const int piece = item / a.num_kv_heads;
+    const int2 code = pieces[piece];
+    it.s = static_cast<int>(static_cast<uint32_t>(code.x) >> 16);
+    it.split = code.x & 0xffff;
+    it.g = item - piece * a.num_kv_heads;
+    it.ctx = code.y;
+    it.nsplit = (it.ctx + a.split_tokens - 1) / a.split_tokens;
+  };
+  int cur_i = blockIdx.x, nxt_i = blockIdx.x + gridDim.x;
+  if (cur_i >= total) return;  // uniform over the workgroup
+  DecItem<HD> cur, nxt;
+  find(cur_i, cur);
+  decode_item_prologue<HD, CHECK>(a, cur);
+  // `fetched` alternates slots: slot p is written before the barrier that ends an item and read
+  // right after it; the next write to slot p comes after one more barrier.
+  for (int p = 0;; p ^= 1) {
+    const bool have_next = nxt_i < total;
+    int after = total;
+    if (have_next) {
+      if (tid == 0) after = atomicAdd(&plan[queue * kCounterStride], 1) * queues + queue;  // returns while this item runs
+      find(nxt_i, nxt);
+      decode_item_prologue<HD, CHECK>(a, nxt);  // in flight while this item runs
     }
-    base += chunk_total;
+    if (cur.ctx == 0) {
+      for (int i = tid; i < a.group * HD; i += kDecThreads)
+        store_out(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + cur.g * a.group) * HD + i, 0.f, a.out_bf16);
+    } else {
+      decode_bf16_item<HD, CHECK, NARROW>(a, cur, smem);
+    }
+    if (tid == 0) fetched[p] = after;
+    __syncthreads();  // the next item reuses the staging and merge areas; fetched[p] is published
+    if (!have_next) break;
+    cur = nxt;
+    nxt_i = fetched[p];
   }
 }
 
@@ -520,37 +561,60 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   ctx = ctx < 0 ? 0 : (ctx > max_blocks * kBlockSize ? max_blocks * kBlockSize : ctx);
   const int nsplit = (ctx + split_tokens - 1) / split_tokens;
   if (nsplit <= 1) return;
-  for (int i = threadIdx.x; i < group * head_dim; i += blockDim.x) {
-    const int h = g * group + i / head_dim, d = i % head_dim;
+  // Each thread owns four consecutive head_dim elements of one query head (16-byte loads).
+  const int quads = head_dim / 4;
+  for (int i = threadIdx.x; i < group * quads; i += blockDim.x) {
+    const int hn = i / quads, d = 4 * (i - hn * quads);
+    const int h = g * group + hn;
     const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_splits;
     // One pass with a running max; the loads of a batch of splits are independent and issue together.
-    float M = -INFINITY, O = 0.f, L = 0.f;
+    float M = -INFINITY, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int p0 = 0; p0 < nsplit; p0 += 8) {
-      float mp[8], lp[8], op[8];
+      float2 ml[8];
+      float4 op[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const bool live = p0 + k < nsplit;
         const int64_t part = base + (live ? p0 + k : p0);
-        mp[k] = live ? ws_ml[part * 2] : -INFINITY;
-        lp[k] = ws_ml[part * 2 + 1];
-        op[k] = ws_o[part * head_dim + d];
+        ml[k] = *reinterpret_cast<const float2*>(ws_ml + part * 2);
+        if (!live) ml[k].x = -INFINITY;
+        op[k] = *reinterpret_cast<const float4*>(ws_o + part * head_dim + d);
       }
       float Mn = M;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mp[k]);
+      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, ml[k].x);
       if (Mn == -INFINITY) continue;
-      const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
-      O *= a;
-      L *= a;
+      const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+      O.x *= sc;
+      O.y *= sc;
+      O.z *= sc;
+      O.w *= sc;
+      L *= sc;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float f = (mp[k] == -INFINITY) ? 0.f : fast_exp2(mp[k] - Mn);
-        O += f * op[k];
-        L += f * lp[k];
+        const float f = (ml[k].x == -INFINITY) ? 0.f : fast_exp2(ml[k].x - Mn);
+        O.x += f * op[k].x;
+        O.y += f * op[k].y;
+        O.z += f * op[k].z;
+        O.w += f * op[k].w;
+        L += f * ml[k].y;
       }
       M = Mn;
     }
-    store_out(out, (static_cast<int64_t>(s) * num_q_heads + h) * head_dim + d, L > 0.f ? O / L : 0.f, out_bf16 != 0);
+    if (L > 0.f) {
+      O.x /= L;
+      O.y /= L;
+      O.z /= L;
+      O.w /= L;
+    } else {
+      O = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int64_t o = (static_cast<int64_t>(s) * num_q_heads + h) * head_dim + d;
+    if (out_bf16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = uint2{pack_bf16x2(O.x, O.y), pack_bf16x2(O.z, O.w)};
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = O;
   }
 }
 
@@ -580,10 +644,23 @@ int32_t resolve_split(int32_t requested, int32_t num_seqs, int32_t hq, int32_t h
   return pkv_decode_split_tokens(num_seqs, hq, hkv, hd, max_blocks);
 }
 
-size_t partial_bytes(int32_t num_seqs, int32_t hq, int32_t hd, int32_t max_splits) {
-  const size_t rows = static_cast<size_t>(num_seqs) * hq * max_splits;
-  const size_t o = (rows * hd * 4 + 255) / 256 * 256;
-  return o + rows * 2 * 4;
+// Workspace: the plan (header ints, then 8 bytes per (sequence, split) piece), then, when a
+// sequence can span several splits, the fp32 partial rows [num_seqs][hq][max_splits][hd] and
+// their (max, normaliser) pairs.  Every part starts on a 256-byte boundary.
+struct WsLayout {
+  size_t pieces, o, ml, total;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+WsLayout ws_layout(int32_t num_seqs, int32_t hq, int32_t hd, int64_t max_splits) {
+  WsLayout w;
+  w.pieces = round256(kPlanInts * 4);
+  w.o = w.pieces + round256(static_cast<size_t>(num_seqs) * max_splits * 8);
+  const size_t rows = max_splits > 1 ? static_cast<size_t>(num_seqs) * hq * max_splits : 0;
+  w.ml = w.o + round256(rows * hd * 4);
+  w.total = w.ml + rows * 2 * 4;
+  return w;
 }
 
 }  // namespace
@@ -594,10 +671,12 @@ extern "C" int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 512;
   const int64_t max_ctx = static_cast<int64_t>(max_blocks_per_seq) * kBlockSize;
   const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  // Prefer long splits (fewer partials, fewer merges) while the largest possible number of work
-  // items still fills two workgroups per CU.
+  // Prefer long splits (fewer partials, fewer merges; the longest-first dynamic schedule evens
+  // out the workgroups) while the largest possible number of work items still covers every
+  // resident workgroup of a 256-CU device (two per CU at head_dim <= 128, one at 256).
+  const int64_t resident = head_dim <= 128 ? 512 : 256;
   for (int S : {2048, 1024, 512, 256})
-    if (pairs * ((max_ctx + S - 1) / S) >= 512) return S;
+    if (pairs * ((max_ctx + S - 1) / S) >= resident) return S;
   return 128;
 }
 
@@ -607,8 +686,7 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
   if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 2048) return 0;
   const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
   const int64_t max_splits = (static_cast<int64_t>(max_blocks_per_seq) * kBlockSize + S - 1) / S;
-  if (max_splits <= 1) return 0;
-  return partial_bytes(num_seqs, num_q_heads, head_dim, static_cast<int32_t>(max_splits));
+  return ws_layout(num_seqs, num_q_heads, head_dim, max_splits).total;
 }
 
 extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
@@ -629,16 +707,21 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
   if (num_seqs == 0) return PKV_OK;
   if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid y/z limits
   if (!out || !query || !key_pool || !value_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  for (const void* p : {static_cast<const void*>(out), query, key_pool, value_pool, static_cast<const void*>(workspace)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARG;
   const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
   const int64_t max_splits64 = (static_cast<int64_t>(max_blocks_per_seq) * kBlockSize + S - 1) / S;
   if (max_splits64 > 65535) return PKV_ERR_UNSUPPORTED;
   const int max_splits = static_cast<int>(max_splits64);
-  const size_t need = max_splits > 1 ? partial_bytes(num_seqs, num_q_heads, head_dim, max_splits) : 0;
-  if (workspace_bytes < need || (need > 0 && !workspace)) return PKV_ERR_WORKSPACE_TOO_SMALL;
-  float* ws_o = static_cast<float*>(workspace);
-  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * max_splits;
-  float* ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + (rows * head_dim * 4 + 255) / 256 * 256)
-                      : nullptr;
+  // Work items index pieces x KV heads in int32.
+  if (static_cast<int64_t>(num_seqs) * max_splits * num_kv_heads > INT32_MAX / 2) return PKV_ERR_UNSUPPORTED;
+  const WsLayout lay = ws_layout(num_seqs, num_q_heads, head_dim, max_splits);
+  if (!workspace || workspace_bytes < lay.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* plan = reinterpret_cast<int32_t*>(ws);
+  int2* pieces = reinterpret_cast<int2*>(ws + lay.pieces);
+  float* ws_o = max_splits > 1 ? reinterpret_cast<float*>(ws + lay.o) : nullptr;
+  float* ws_ml = max_splits > 1 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
   const int group = num_q_heads / num_kv_heads;
   const float scale_log2 = scale * kLog2e;
   const int ob = out_dtype == PKV_DTYPE_BF16;
@@ -664,11 +747,20 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
     // workgroups than the largest possible number of items.
     const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * max_splits;
     const int64_t resident = static_cast<int64_t>(pkv_host::cu_count()) * (head_dim <= 128 ? 2 : 1);
-    const dim3 pgrid(static_cast<unsigned>(max_items < resident ? max_items : resident));
+    const unsigned nwg = static_cast<unsigned>(max_items < resident ? max_items : resident);
+    const int queues = nwg % kMaxQueues == 0 ? kMaxQueues : (nwg % 8 == 0 ? 8 : 1);
     const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
                         num_blocks < (1 << 24);
-#define PKV_DEC_BF16(HD, CHECK, NARROW) \
-  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW>), pgrid, dim3(kDecThreads), 0, st, a, num_seqs)
+    if (err_flag)
+      hipLaunchKernelGGL((decode_plan_kernel<true>), dim3(1), dim3(kPlanThreads), 0, st, context_lens, num_seqs,
+                         max_blocks_per_seq, S, pieces, plan, static_cast<int>(nwg), queues, err_flag);
+    else
+      hipLaunchKernelGGL((decode_plan_kernel<false>), dim3(1), dim3(kPlanThreads), 0, st, context_lens, num_seqs,
+                         max_blocks_per_seq, S, pieces, plan, static_cast<int>(nwg), queues, err_flag);
+    if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+#define PKV_DEC_BF16(HD, CHECK, NARROW)                                                                    \
+  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW>), dim3(nwg), dim3(kDecThreads), 0, st, a, pieces, \
+                     plan, queues)
 #define PKV_DEC_BF16_N(HD, CHECK) \
   if (narrow) PKV_DEC_BF16(HD, CHECK, true); else PKV_DEC_BF16(HD, CHECK, false);
 #define PKV_DEC_BF16_C(HD) \

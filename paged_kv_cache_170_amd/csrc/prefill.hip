@@ -368,6 +368,8 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
   if (num_blocks == 0) return PKV_ERR_INVALID_ARG;  // a non-empty chunk needs cached positions
   if (!out || !query || !cu_q_lens || !chunk_offsets || !key_pool || !value_pool || !block_tables)
     return PKV_ERR_INVALID_ARG;
+  for (const void* p : {static_cast<const void*>(out), query, key_pool, value_pool})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARG;
   const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
   const int64_t items = static_cast<int64_t>(num_seqs) * num_q_heads * q_tiles;
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;

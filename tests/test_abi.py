@@ -47,8 +47,10 @@ def test_split_and_workspace_queries():
     ws = pkv.decode_workspace_bytes(128, 64, 8, 128, 512)
     nsplit = -(-512 * 16 // s)
     assert ws >= 128 * 64 * nsplit * (128 + 2) * 4
-    # One split: no workspace needed.
-    assert pkv.decode_workspace_bytes(4, 8, 8, 64, 8, 128) == 0
+    # One split: only the work plan (a small header, then 8 bytes per sequence, in 256-byte units).
+    one = pkv.decode_workspace_bytes(4, 8, 8, 64, 8, 128)
+    assert 0 < one < 65536 and one % 256 == 0
+    assert pkv.decode_workspace_bytes(40, 8, 8, 64, 8, 128) == one + 256
     # Invalid shapes report zero.
     assert pkv.decode_workspace_bytes(4, 8, 3, 64, 8, 0) == 0
     assert pkv.decode_workspace_bytes(4, 8, 8, 96, 8, 0) == 0
@@ -69,7 +71,7 @@ def test_host_validation_rejects_bad_arguments():
     assert dec(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 1, 100, null, 0, null, null) == 1
     assert dec(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 1, 0, null, 0, null, null) == 1
     fake = ctypes.c_void_p(16)
-    # A 64-block table needs several splits at split 128 -> workspace required.
+    # The workspace is always required (it holds the work plan).
     assert dec(fake, 0, fake, fake, fake, fake, 64, fake, 2, 8, 8, 64, 10, 0.1, 1, 128, null, 0, null, null) == 3
     # Empty batch is a no-op.
     assert dec(null, 0, null, null, null, null, 8, null, 0, 8, 8, 64, 10, 0.1, 1, 0, null, 0, null, null) == 0
