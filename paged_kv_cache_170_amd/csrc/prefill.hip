@@ -23,6 +23,9 @@
 //     accumulator rescale off the common path.
 //   * P stays in registers and is exactly the B operand of O^T = V^T P^T; V^T comes from the
 //     natural-layout V tile through ds_read_b64_tr_b16.
+//   * consecutive MFMAs work on different accumulators, and the LDS operand reads are scheduled
+//     four (K) or eight (V) reads ahead of the MFMAs that use them, so MFMA issue does not wait on
+//     LDS latency.
 #include <cmath>
 
 #include "common.hpp"
@@ -49,7 +52,6 @@ struct PreCfg {
   static constexpr int TILE = KT * (KPITCH + VPITCH);
   static constexpr int LOADS = 2 * KT * CPR / kPreThreads;  // chunks per thread per tensor per tile pair
   static constexpr int LDS = 4 * TILE;                       // two buffers of a tile pair
-  static constexpr int LINES = 2 * KT * (HD * 2 / 128);      // 128-byte lines per tensor per tile pair
   static constexpr int COMB = 4 * kPreRows * HD * 4 + 2 * 4 * kPreRows * 4;
   static_assert(LDS >= COMB, "merge area must fit in the tile buffers");
   static_assert(LOADS * kPreThreads == 2 * KT * CPR, "pair loads must divide evenly");
@@ -155,21 +157,6 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       }
     }
   };
-  // One 4-byte read per 128-byte line of pair p: pulls the pair into L2 ahead of its gather.  The
-  // value is folded into a sink one pair later, so nothing waits on it.
-  constexpr int LPRL = HD * 2 / 128;  // lines per row
-  auto touch_pair = [&](int p) -> uint32_t {
-    const int line = threadIdx.x;
-    if (line >= 2 * C::LINES) return 0u;
-    const int tensor = line / C::LINES, rem = line - tensor * C::LINES;
-    const int key = 2 * p * C::KT + rem / LPRL;
-    if (key >= kv_end) return 0u;
-    const int b = ids[key / kBlockSize - win0];
-    if (b < 0) return 0u;
-    const uint16_t* base = tensor ? value_pool : key_pool;
-    const uint32_t cb = static_cast<uint32_t>(((key % kBlockSize) * num_kv_heads + g) * HD * 2 + (rem % LPRL) * 128);
-    return *reinterpret_cast<const uint32_t*>(pool_at<NARROW>(base, b, blk_bytes, cb));
-  };
   auto store_pair = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
@@ -188,7 +175,6 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
   fill_ids(0);
   __syncthreads();
   load_pair(0);
-  uint32_t touched = npairs > 1 ? touch_pair(1) : 0u, touch_sink = 0u;
   store_pair(0);
   __syncthreads();
 
@@ -204,24 +190,35 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       __syncthreads();
     }
     if (pr + 1 < npairs) load_pair(pr + 1);
-    const uint32_t touch_next = pr + 2 < npairs ? touch_pair(pr + 2) : 0u;
     const int kt = 2 * pr + grp;
     const int key0 = kt * C::KT;
     const bool active = kt < ntiles && wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
     if (active) {
       const char* tile = smem + (2 * cur + grp) * C::TILE;
       floatx16 sacc[C::MS];
+      // The MS accumulators are interleaved so that consecutive MFMAs are independent.
 #pragma unroll
       for (int ms = 0; ms < C::MS; ++ms) {
         const char* krow = tile + (32 * ms + qc) * C::KPITCH + 16 * hh;
         sacc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow), qf[0],
                                                            floatx16{}, 0, 0, 0);
+      }
 #pragma unroll
-        for (int ks = 1; ks < C::KS; ++ks) {
+      for (int ks = 1; ks < C::KS; ++ks)
+#pragma unroll
+        for (int ms = 0; ms < C::MS; ++ms) {
+          const char* krow = tile + (32 * ms + qc) * C::KPITCH + 16 * hh;
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
           sacc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[ms], 0, 0, 0);
         }
+      // Keep four K reads in flight ahead of the MFMAs that consume them.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < C::MS * C::KS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // Element e = 4i + j of sacc[ms] is key key0 + 32ms + 8i + 4hh + j for query row qc.  Only
       // tiles that cross the causal diagonal or the end of the keys need the mask.
       const bool edge = key0 + C::KT > kv_end || (causal && key0 + C::KT - 1 > off + wrow0);
@@ -253,7 +250,6 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
         for (int md = 0; md < C::MD; ++md) acc[md] *= alpha;
       }
       // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
-      // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
       const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
       // p = 2^(s * scale * log2e - m_ref), rounded to bf16 pairs: these are both the B operand of the
       // P.V product and, summed in fp32, the row normaliser (so numerator and denominator use the
@@ -279,23 +275,29 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       // O^T += V^T P^T.  k-step a covers keys 16a + 4hh + e and 16a + 8 + 4hh + e (e = 0..3),
       // matching pb[a]; the A operand lane (l % 32 = d, hh) reads those keys' V at d.
       const uint16_t* vbase = reinterpret_cast<const uint16_t*>(tile + C::KT * C::KPITCH);
+      // The MD accumulators are interleaved so that consecutive MFMAs are independent.
 #pragma unroll
-      for (int md = 0; md < C::MD; ++md) {
-        const int col = 32 * md + 16 * dg + 4 * (li & 3);
+      for (int a = 0; a < C::KA; ++a) {
+        const int r0 = 16 * a + 4 * hh + (li >> 2);
 #pragma unroll
-        for (int a = 0; a < C::KA; ++a) {
-          const int r0 = 16 * a + 4 * hh + (li >> 2);
+        for (int md = 0; md < C::MD; ++md) {
+          const int col = 32 * md + 16 * dg + 4 * (li & 3);
           const bf16x8 av = concat(lds_read_tr16(vbase + r0 * VP + col), lds_read_tr16(vbase + (r0 + 8) * VP + col));
           acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[a], acc[md], 0, 0, 0);
         }
       }
+      // Keep eight transposed V reads (four MFMA operands) in flight ahead of their MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < C::MD * C::KA - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     if (pr + 1 < npairs) store_pair(cur ^ 1);
-    touch_sink ^= touched;  // issued before this pair's gathers, so already complete
-    touched = touch_next;
     __syncthreads();
   }
-  if (touch_sink == 0x9e3779b9u && causal == 0x5eed) m_ref += 1.f;  // keeps the touches alive
 
   // Merge the two key groups: group 1 parks its state in LDS, group 0 combines and writes.
   l_run += __shfl_xor(l_run, 32);
