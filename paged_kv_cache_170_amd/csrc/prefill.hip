@@ -17,10 +17,10 @@
 //     table by all 512 threads, a pair at a time, into double-buffered LDS; the next pair's loads
 //     are in flight while the current pair is computed, with one barrier per pair.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows in registers);
-//     the accumulator layout gives each lane 16 keys of one query, so the row max needs one
-//     cross-lane step.  Only tiles crossing the causal diagonal or the key end are masked, and the
-//     running max is moved lazily (only when a tile max exceeds it by 2^8), which keeps the
-//     accumulator rescale off the common path.
+//     the accumulator layout gives each lane 16 keys of one query.  Only tiles crossing the causal
+//     diagonal or the key end are masked.  The reference max the exponentials subtract trails the
+//     running max: it is raised (with the accumulator rescale) only when a weight would exceed
+//     2^20, on edge tiles, or before the first key, so the common path computes no row max.
 //   * P stays in registers and is exactly the B operand of O^T = V^T P^T; V^T comes from the
 //     natural-layout V tile through ds_read_b64_tr_b16.
 //   * consecutive MFMAs work on different accumulators, and the LDS operand reads are scheduled
@@ -36,7 +36,7 @@ constexpr int kPreWaves = 8;                    // two groups of four waves
 constexpr int kPreThreads = kPreWaves * kWave;
 constexpr int kPreRows = 32;                    // query rows per wave
 constexpr int kPreTile = 4 * kPreRows;          // query rows per workgroup
-constexpr float kRescaleGap = 8.f;              // log2 units the running max may trail the tile max
+constexpr float kMaxWeight = 1048576.f;         // 2^20: largest softmax weight before the reference max moves
 constexpr int kIdWindow = 2048;                 // block ids held in LDS (32,768 positions)
 
 template <int HD>
@@ -232,41 +232,47 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
             sacc[ms][e] = ok ? sacc[ms][e] : -INFINITY;
           }
       }
-      float mx = -INFINITY;
+      // Softmax weights.  The reference max m_ref trails the running max: it is raised only when a
+      // weight of this tile would exceed 2^20 (or no key was seen yet) or on edge tiles, so the
+      // common path computes no row max.  m_ref only matters through rounding.
+      auto raise_max = [&]() {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int ms = 0; ms < C::MS; ++ms)
+        for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[ms][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lazy rescale: the reference max moves only when the tile max exceeds it by kRescaleGap,
-      // so probabilities stay below 2^kRescaleGap and the accumulators are rarely touched.
-      const float m_tile = mx * scale_log2;
-      const bool need = m_tile > m_ref + kRescaleGap;
-      if (__any(need)) {
-        const float alpha = need ? fast_exp2(m_ref - m_tile) : 1.f;
-        m_ref = need ? m_tile : m_ref;
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[ms][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = mx * scale_log2;
+        const bool up = m_new > m_ref;
+        const float alpha = up ? (m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new)) : 1.f;
+        m_ref = up ? m_new : m_ref;
         l_run *= alpha;
 #pragma unroll
         for (int md = 0; md < C::MD; ++md) acc[md] *= alpha;
-      }
-      // A row that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
-      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      // p = 2^(s * scale * log2e - m_ref), rounded to bf16 pairs: these are both the B operand of the
-      // P.V product and, summed in fp32, the row normaliser (so numerator and denominator use the
-      // same rounded weights).
+      };
       uint32_t pw[C::MS * 8];
-      float ps0 = 0.f, ps1 = 0.f;
+      auto expo = [&]() {
+        const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int ms = 0; ms < C::MS; ++ms)
+        for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[ms][2 * q], scale_log2, neg_m));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[ms][2 * q + 1], scale_log2, neg_m));
-          const uint32_t w = pack_bf16x2(p0, p1);
-          pw[ms * 8 + q] = w;
-          if (q & 1) ps1 = add_bf16x2(w, ps1); else ps0 = add_bf16x2(w, ps0);
-        }
-      l_run += ps0 + ps1;
+          for (int q = 0; q < 8; ++q) {
+            const float p0 = fast_exp2(__builtin_fmaf(sacc[ms][2 * q], scale_log2, neg_m));
+            const float p1 = fast_exp2(__builtin_fmaf(sacc[ms][2 * q + 1], scale_log2, neg_m));
+            const uint32_t w = pack_bf16x2(p0, p1);
+            pw[ms * 8 + q] = w;
+            if (q & 1) ps1 = add_bf16x2(w, ps1); else ps0 = add_bf16x2(w, ps0);
+          }
+        return ps0 + ps1;
+      };
+      if (edge) raise_max();
+      float ps = expo();
+      if (__any(!(ps < kMaxWeight) || m_ref == -INFINITY)) {
+        raise_max();
+        ps = expo();
+      }
+      l_run += ps;
       bf16x8 pb[C::KA];
 #pragma unroll
       for (int a = 0; a < C::KA; ++a)
