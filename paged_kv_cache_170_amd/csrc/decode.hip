@@ -16,8 +16,9 @@
 //     S^T = K Q^T uses v_mfma_f32_16x16x32_bf16 with the 16 MFMA columns holding the G query
 //     heads (zero-padded), and V is read back transposed with ds_read_b64_tr_b16 as the A operand
 //     of O^T = V^T P^T.
-//   * the online softmax runs in the log2 domain on the MFMA accumulator layout; the 4 waves'
-//     states merge in LDS, and a split's (o, m, l) goes to the workspace unless the sequence
+//   * the online softmax runs in the log2 domain on the MFMA accumulator layout against a
+//     reference max that is raised only when a weight would pass 2^20 (so the common step needs
+//     no cross-lane max); the 4 waves' states merge in LDS, and a split's (o, m, l) goes to the workspace unless the sequence
 //     fits one split, in which case the normalised row is written directly.
 //   * fp32 pools take a plain VALU kernel with the same split/merge structure.
 #include <cstdlib>
@@ -30,7 +31,7 @@ namespace pkv {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kMaxGroup = 16;
-constexpr float kRescaleGap = 8.f;  // log2 units the running max may trail a step's max
+constexpr float kMaxWeight = 1048576.f;  // 2^20: largest softmax weight before the reference max moves
 
 template <int HD>
 struct DecCfg {
@@ -233,8 +234,9 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
         sacc[pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(krow + 64 * kk), qf[kk],
                                                            sacc[pg], 0, 0, 0);
     }
-    // Online softmax (log2 domain, scale folded into the exponent's FMA).
-    float mx = -INFINITY;
+    // Online softmax (log2 domain, scale folded into the exponent's FMA).  The reference max m_ref
+    // trails the running max and is raised only when a weight would pass 2^20 (or before the first
+    // key), so the common path needs no cross-lane max.
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       const bool blk_ok = (pg ? B.b1 : B.b0) >= 0;
@@ -242,32 +244,41 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
       for (int j = 0; j < 4; ++j) {
         const int tok = t0 + pg * kBlockSize + 4 * c + j;
         sacc[pg][j] = (blk_ok && tok < ctx) ? sacc[pg][j] : -INFINITY;
-        mx = fmaxf(mx, sacc[pg][j]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_tile = mx * scale_log2;
-    const bool need = m_tile > m_ref + kRescaleGap;
-    if (__any(need)) {
-      const float alpha = need ? fast_exp2(m_ref - m_tile) : 1.f;
-      m_ref = need ? m_tile : m_ref;
+    uint32_t pw[4];
+    auto expo = [&]() {
+      // A head that has seen no valid key yet keeps m_ref = -inf; its scores are used as they are.
+      const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[pg][2 * q], scale_log2, neg_m));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[pg][2 * q + 1], scale_log2, neg_m));
+          pw[2 * pg + q] = pack_bf16x2(p0, p1);
+        }
+      return add_bf16x2(pw[0], add_bf16x2(pw[1], add_bf16x2(pw[2], add_bf16x2(pw[3], 0.f))));
+    };
+    float ps = expo();
+    if (__any(!(ps < kMaxWeight) || m_ref == -INFINITY)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[pg][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = mx * scale_log2;
+      const bool up = m_new > m_ref;
+      const float alpha = up ? (m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new)) : 1.f;
+      m_ref = up ? m_new : m_ref;
       l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) acc[mt] *= alpha;
+      ps = expo();
     }
-    // A head that has seen no valid key yet keeps m_ref = -inf; its masked scores must still give 0.
-    const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-    uint32_t pw[4];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float p0 = fast_exp2(__builtin_fmaf(sacc[pg][2 * q], scale_log2, neg_m));
-        const float p1 = fast_exp2(__builtin_fmaf(sacc[pg][2 * q + 1], scale_log2, neg_m));
-        pw[2 * pg + q] = pack_bf16x2(p0, p1);
-      }
-    l_run = add_bf16x2(pw[0], add_bf16x2(pw[1], add_bf16x2(pw[2], add_bf16x2(pw[3], l_run))));
+    l_run += ps;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, uint4{pw[0], pw[1], pw[2], pw[3]});
 
     // O^T += V^T P^T.  A operand: lane (n, c) needs V[token 4c+e][d = 16mt + n] of both blocks.
