@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed_step", choices=["mixed_step", "gqa_decode", "long_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra untimed-for-value steps, each after a 1 GiB write that flushes L2 and MALL")
     ap.add_argument("--cpu-sample-rows", type=int, default=64, help="prefill rows timed in the oracle baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain fp32 copy kernel over this many MiB (a known-size reference "
@@ -215,6 +217,24 @@ def main():
     print(f"[bench] {args.steps} steps in {wall:.3f}s; per-kernel avg ms "
           + ", ".join(f"{n}={avg_ms[n]:.4f}" for n in names), file=sys.stderr, flush=True)
 
+    def spread(v):
+        return {"p10": float(np.percentile(v, 10)), "p50": float(np.median(v)), "p90": float(np.percentile(v, 90))}
+
+    # Cold-cache timings (outside the timed region): before each step a 1 GiB write evicts the
+    # L2s and the 256 MB MALL, so every kernel starts from HBM.
+    cold = {n: [] for n in names}
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_steps)]
+        for k in range(args.cold_steps):
+            flush.zero_()
+            step(cev[k])
+        torch.cuda.synchronize()
+        for ev in cev:
+            for i, n in enumerate(names):
+                cold[n].append(ev[i].elapsed_time(ev[i + 1]))
+        del flush
+
     # Bandwidth a plain read stream reaches on this device: read the whole key pool (>= 1 GB).
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     for _ in range(2):
@@ -240,12 +260,19 @@ def main():
         "stream_read_gbs": stream_gbs,
         "decode_frac_of_stream_read": dec_gbs / stream_gbs,
     }
+    ran = [n for n in names if (has_write or n not in ("slot_mapping", "cache_write")) and (pre is not None or n != "prefill")]
+    secondary["kernel_ms_hot"] = {n: spread(per[n]) for n in ran}
+    if args.cold_steps > 0:
+        secondary["kernel_ms_cold"] = {n: spread(cold[n]) for n in ran}
+        secondary["decode_gbs_unique_cold"] = dec_bytes / (float(np.median(cold["decode"])) * 1e-3) / 1e9
     kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs, HBM_PEAK_GBS, "GB/s", "decode.hip")}
     if pre is not None:
         fl = prefill_flops(pre)
         pre_tf = fl / (avg_ms["prefill"] * 1e-3) / 1e12
         secondary.update({"prefill_ms": avg_ms["prefill"], "prefill_flop": fl, "prefill_tflops": pre_tf,
                           "prefill_frac_mfma_peak": pre_tf / BF16_MFMA_PEAK_TFLOPS})
+        if args.cold_steps > 0:
+            secondary["prefill_tflops_cold"] = fl / (float(np.median(cold["prefill"])) * 1e-3) / 1e12
         kernels["prefill"] = (avg_ms["prefill"], "mfma", fl, pre_tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s", "prefill.hip")
     if has_write:
         wb = 2 * wcase.num_new_tokens * wcase.num_kv_heads * wcase.head_dim * wcase.elem_bytes * 2 + 4 * wcase.num_new_tokens
