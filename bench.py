@@ -247,6 +247,39 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = 5 * kp.numel() * kp.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
+    # Copy-on-write block copies on this pool: 512 disjoint pairs (K and V, read + written).
+    nblk = dec.num_blocks
+    cp = torch.randperm(nblk, device="cpu")[:1024].to(torch.int32)
+    c_src, c_dst = cp[:512].to(dev), cp[512:].to(dev)
+    for _ in range(2):
+        pkv.copy_blocks(kp, vp, c_src, c_dst)
+    e0.record(stream)
+    for _ in range(10):
+        pkv.copy_blocks(kp, vp, c_src, c_dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / 10
+    block_bytes = kp[0].numel() * kp.element_size()
+    copy_info = {"pairs": 512, "ms": copy_ms, "gbs": 4 * 512 * block_bytes / (copy_ms * 1e-3) / 1e9}
+
+    # Host-side block manager on the decode batch's shape: every sequence is added (a shared
+    # prefix of 63 full blocks, as in the mixed step), extended by one decode token, and freed.
+    bm = pkv.BlockManager(nblk)
+    rows = np.full((dec.num_seqs, dec.max_blocks_per_seq), -1, np.int32)
+    prefix = np.arange(63 * 16, dtype=np.int32)
+    prompts = [np.concatenate([prefix, np.full(max(int(c) - 1 - prefix.size, 0), 100000 + s, np.int32)])[: int(c) - 1]
+               for s, c in enumerate(dec.context_lens)]
+    t_bm = time.perf_counter()
+    hits = 0
+    for s in range(dec.num_seqs):
+        hits += bm.add_sequence(prompts[s], rows[s]) > 0
+    for s in range(dec.num_seqs):
+        bm.append(rows[s], prompts[s].size, 1)
+    for s in range(dec.num_seqs):
+        bm.free_sequence(rows[s], prompts[s].size + 1)
+    bm_us = (time.perf_counter() - t_bm) * 1e6 / (3 * dec.num_seqs)
+    bm_info = {"sequences": dec.num_seqs, "prefix_hits": hits, "us_per_operation": bm_us}
+
     dec_bytes, dec_kv_unique, dec_kv_logical = decode_algorithmic_bytes(dec)
     dec_s = avg_ms["decode"] * 1e-3
     dec_gbs = dec_bytes / dec_s / 1e9
@@ -259,6 +292,8 @@ def main():
         "decode_kv_bytes_logical": dec_kv_logical,
         "stream_read_gbs": stream_gbs,
         "decode_frac_of_stream_read": dec_gbs / stream_gbs,
+        "copy_blocks": copy_info,
+        "block_manager_host": bm_info,
     }
     ran = [n for n in names if (has_write or n not in ("slot_mapping", "cache_write")) and (pre is not None or n != "prefill")]
     secondary["kernel_ms_hot"] = {n: spread(per[n]) for n in ran}

@@ -15,8 +15,14 @@
  *                     cached K/V of all earlier chunks plus its own tokens (section on how chunked
  *                     prefill works, with its PyTorch example).
  *   [Engine-core]     "第2章:推理引擎核心技术" (aiinfra.vidrealm.tech), §1.2 (block-table example:
- *                     logical block j holds tokens 16j..16j+15) and §1.4 (the paged kernel walks a
- *                     request's pages through the table and accumulates with an online softmax).
+ *                     logical block j holds tokens 16j..16j+15), §1.4 (the paged kernel walks a
+ *                     request's pages through the table and accumulates with an online softmax),
+ *                     §1.5 (copy-on-write: sequences share pages and copy one only where they
+ *                     diverge) and §3.2 (prefix cache: hash each page of a prompt's tokens, share
+ *                     the physical page on a hit by raising its reference count).
+ *   [C13-L2] also, same section: paging wastes at most b - 1 token slots per request and has no
+ *                     external fragmentation; several sequences may point at the same blocks and a
+ *                     shared block is copied only when one of them writes into it.
  *
  * Data layout shared by every call (all device memory, caller-owned):
  *   key_pool, value_pool  [num_blocks, 16, num_kv_heads, head_dim], row-major, same dtype.  A
@@ -32,7 +38,8 @@
  *   - Device pointers are device memory; int arguments are host values.  `stream` is a
  *     hipStream_t (NULL = the null stream).  Every call only enqueues work on `stream` and returns;
  *     buffers must stay alive until the stream reaches the call.  No call synchronises, allocates
- *     or keeps state between calls (the only cached state is each device's compute-unit count).
+ *     or keeps state between calls (the only cached state is each device's compute-unit count);
+ *     the block manager (pkv_bm_*) is host code whose state lives in a caller-owned host buffer.
  *   - Calls return a pkv_status.  Argument errors are found on the host before any HIP call.
  *     PKV_ERR_HIP reports a failed launch (hipGetLastError).  No C++ exception crosses the ABI.
  *   - err_flag: if non-NULL (a device int32, zeroed by the caller), kernels check every block id
@@ -63,7 +70,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1,         /* null pointer, negative size, inconsistent shapes */
   PKV_ERR_UNSUPPORTED = 2,         /* dtype, head_dim, head ratio or block size outside the list above */
   PKV_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below pkv_decode_workspace_bytes() */
-  PKV_ERR_HIP = 4                  /* a kernel launch failed */
+  PKV_ERR_HIP = 4,                 /* a kernel launch failed */
+  PKV_ERR_NO_SPACE = 5             /* block manager: not enough free blocks (state left unchanged) */
 } pkv_status;
 
 typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1 } pkv_dtype;
@@ -186,6 +194,71 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
                                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t num_blocks, int32_t causal, float scale,
                                         pkv_dtype dtype, int32_t* err_flag, void* stream);
+
+/*
+ * Block copy for copy-on-write ([Engine-core] §1.5; [C13-L2] 改进二, sharing paragraph): for each
+ * pair i, the whole block src[i] (16 rows x num_kv_heads x head_dim, K and V) is copied bit for bit
+ * to block dst[i].  src / dst: int32 [num_pairs] device arrays; src[i] == dst[i] is a no-op; a
+ * block that is a destination must not be a source or destination of another pair in the same call
+ * (undefined otherwise).  dtype F32 or BF16 (a bit copy either way).  With err_flag, ids outside
+ * [0, num_blocks) set PKV_FLAG_BAD_BLOCK and that pair is skipped.
+ */
+pkv_status pkv_copy_blocks(void* key_pool, void* value_pool, const int32_t* src, const int32_t* dst,
+                           int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, pkv_dtype dtype, int32_t* err_flag, void* stream);
+
+/*
+ * Block manager (host code; every pointer below is host memory).  It hands out physical blocks of
+ * one pool to sequences and fills their block-table rows ([Engine-core] §1.2), shares blocks
+ * between sequences with reference counts, finds a new prompt's cached prefix by a chained hash of
+ * each full block's token ids ([Engine-core] §3.2), and copies a shared block before a sequence
+ * writes into it ([Engine-core] §1.5).  Policies the pages leave open (stated readings):
+ *   - free blocks sit in a FIFO queue: allocation takes the front, a freed block goes to the back,
+ *     so the blocks freed longest ago are reused first;
+ *   - the hash of full block j is FNV-1a (64-bit) over the 8 bytes of block j-1's hash (0 for j = 0)
+ *     followed by the block's 16 token ids (4 bytes each, little-endian), with 0 mapped to 1;
+ *   - a prompt's full blocks are registered under their hash when they are allocated (their K/V is
+ *     written by that step's prefill); a freed block keeps its hash while it waits in the queue and
+ *     can be found again until it is handed out for new content;
+ *   - a lookup walks the prompt's full blocks from the start and stops at the first miss.
+ * The state is one caller-owned buffer of pkv_bm_state_bytes(num_blocks) bytes (8-byte aligned);
+ * calls on one state must not overlap (not thread-safe).  Every call validates its arguments and
+ * leaves the state unchanged when it returns an error.
+ */
+size_t pkv_bm_state_bytes(int32_t num_blocks);
+
+/* All blocks free.  free_order: NULL for 0, 1, ..., num_blocks-1, else a permutation of them giving
+ * the initial queue order (e.g. a seeded shuffle).  block_size must be 16. */
+pkv_status pkv_bm_init(void* state, size_t state_bytes, int32_t num_blocks, int32_t block_size,
+                       const int32_t* free_order);
+
+/* New sequence with prompt tokens[0..num_tokens): reuse the blocks of its longest cached prefix of
+ * full blocks, allocate the rest, write table_row[0 .. ceil(num_tokens/16)).  *cached_tokens = the
+ * number of leading tokens whose K/V the reused blocks already hold (a multiple of 16).
+ * PKV_ERR_NO_SPACE if the free queue cannot cover the new blocks. */
+pkv_status pkv_bm_add_sequence(void* state, const int32_t* tokens, int32_t num_tokens, int32_t* table_row,
+                               int32_t max_blocks, int32_t* cached_tokens);
+
+/* Append num_new tokens to a sequence holding ctx tokens: when its last block is partly filled and
+ * shared, it is first replaced by a fresh copy (one pair in copy_src/copy_dst for
+ * pkv_copy_blocks, *num_copies = 1, else 0); new blocks are allocated as positions cross block
+ * boundaries.  slots[i] = slot of position ctx + i (the slot mapping for pkv_cache_write). */
+pkv_status pkv_bm_append(void* state, int32_t* table_row, int32_t max_blocks, int32_t ctx, int32_t num_new,
+                         int32_t* slots, int32_t* copy_src, int32_t* copy_dst, int32_t* num_copies);
+
+/* child_row[0 .. ceil(ctx/16)) = parent_row's blocks, each shared (reference count + 1). */
+pkv_status pkv_bm_fork(void* state, const int32_t* parent_row, int32_t ctx, int32_t* child_row,
+                       int32_t max_blocks);
+
+/* Drop a sequence of ctx tokens: each of its blocks loses one reference; blocks left with none go to
+ * the back of the free queue. */
+pkv_status pkv_bm_free_sequence(void* state, const int32_t* table_row, int32_t ctx);
+
+/* Inspection (for tests and monitoring): free blocks, a block's reference count (-1 if out of
+ * range), a block's registered hash (0 if none). */
+int32_t pkv_bm_num_free(const void* state);
+int32_t pkv_bm_refcount(const void* state, int32_t block);
+uint64_t pkv_bm_block_hash(const void* state, int32_t block);
 
 /*
  * Streaming-read reference (not part of the attention path): reads `bytes` bytes at `buf` (device,

@@ -17,6 +17,7 @@ from .paged_attention import (  # noqa: F401
     decode,
     decode_split_partials,
     gather,
+    kv_head_of,
     prefill_chunk,
     slot_mapping,
     softmax_attention,

@@ -25,7 +25,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = 0, 1, 2, 3, 4
+OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, NO_SPACE = 0, 1, 2, 3, 4, 5
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FLAG_BAD_BLOCK, FLAG_BAD_SLOT, FLAG_BAD_LENGTH = 1, 2, 4
 BLOCK_SIZE = 16
@@ -45,6 +45,16 @@ _SIGS = {
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
     "pkv_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
+    "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_bm_state_bytes": (_sz, [_i32]),
+    "pkv_bm_init": (_i32, [_vp, _sz, _i32, _i32, _vp]),
+    "pkv_bm_add_sequence": (_i32, [_vp, _vp, _i32, _vp, _i32, _vp]),
+    "pkv_bm_append": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "pkv_bm_fork": (_i32, [_vp, _vp, _i32, _vp, _i32]),
+    "pkv_bm_free_sequence": (_i32, [_vp, _vp, _i32]),
+    "pkv_bm_num_free": (_i32, [_vp]),
+    "pkv_bm_refcount": (_i32, [_vp, _i32]),
+    "pkv_bm_block_hash": (ctypes.c_uint64, [_vp, _i32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -140,6 +150,87 @@ def cache_write(key: torch.Tensor, value: torch.Tensor, key_pool: torch.Tensor, 
     _check(_lib.pkv_cache_write(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_pool),
                                 _ptr(value_pool), _ptr(slot_mapping), T, nblk, hkv, hd, bs,
                                 _dtype_code(key_pool), _ptr(err_flag), _stream(key.device)), "pkv_cache_write")
+
+
+def copy_blocks(key_pool: torch.Tensor, value_pool: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
+                err_flag: torch.Tensor | None = None) -> None:
+    """Copy whole blocks src[i] -> dst[i] in both pools (copy-on-write); see pkv_copy_blocks."""
+    _need_gpu(key_pool, value_pool, src, dst, err_flag)
+    _need_i32(src, dst, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    if src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D and the same length")
+    _check(_lib.pkv_copy_blocks(_ptr(key_pool), _ptr(value_pool), _ptr(src), _ptr(dst), src.shape[0], nblk, hkv, hd,
+                                bs, _dtype_code(key_pool), _ptr(err_flag), _stream(key_pool.device)),
+           "pkv_copy_blocks")
+
+
+class BlockManager:
+    """Host-side block manager over one pool (see the pkv_bm_* calls): block tables are rows of a
+    caller-owned int32 numpy array [max_seqs, max_blocks]; the state is a numpy buffer."""
+
+    def __init__(self, num_blocks: int, free_order=None):
+        import numpy as np
+        self._np = np
+        n = int(_lib.pkv_bm_state_bytes(num_blocks))
+        if n == 0:
+            raise ValueError("bad num_blocks")
+        self._state = np.zeros((n + 7) // 8, dtype=np.uint64)
+        fo = None
+        if free_order is not None:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            if fo.shape != (num_blocks,):
+                raise ValueError("free_order must list every block once")
+        self.num_blocks = num_blocks
+        _check(_lib.pkv_bm_init(self._sp(), n, num_blocks, BLOCK_SIZE, self._ap(fo)), "pkv_bm_init")
+
+    def _sp(self):
+        return ctypes.c_void_p(self._state.ctypes.data)
+
+    @staticmethod
+    def _ap(a):
+        return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+    def _row(self, row):
+        if row.dtype != self._np.int32 or not row.flags["C_CONTIGUOUS"] or row.ndim != 1:
+            raise ValueError("table rows must be contiguous 1-D int32 numpy arrays")
+        return row
+
+    def add_sequence(self, tokens, table_row) -> int:
+        """Fill table_row for a new prompt; returns the number of cached (reused) leading tokens."""
+        tok = self._np.ascontiguousarray(tokens, dtype=self._np.int32)
+        row = self._row(table_row)
+        cached = ctypes.c_int32(0)
+        _check(_lib.pkv_bm_add_sequence(self._sp(), self._ap(tok), tok.shape[0], self._ap(row), row.shape[0],
+                                        ctypes.byref(cached)), "pkv_bm_add_sequence")
+        return cached.value
+
+    def append(self, table_row, ctx: int, num_new: int):
+        """Extend a sequence; returns (slots, copy pairs as an [n, 2] int32 array)."""
+        row = self._row(table_row)
+        slots = self._np.empty(max(num_new, 1), dtype=self._np.int32)
+        cs, cd, nc = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(_lib.pkv_bm_append(self._sp(), self._ap(row), row.shape[0], int(ctx), int(num_new), self._ap(slots),
+                                  ctypes.byref(cs), ctypes.byref(cd), ctypes.byref(nc)), "pkv_bm_append")
+        pairs = self._np.array([[cs.value, cd.value]], dtype=self._np.int32)[: nc.value]
+        return slots[:num_new], pairs
+
+    def fork(self, parent_row, ctx: int, child_row) -> None:
+        _check(_lib.pkv_bm_fork(self._sp(), self._ap(self._row(parent_row)), int(ctx), self._ap(self._row(child_row)),
+                                child_row.shape[0]), "pkv_bm_fork")
+
+    def free_sequence(self, table_row, ctx: int) -> None:
+        _check(_lib.pkv_bm_free_sequence(self._sp(), self._ap(self._row(table_row)), int(ctx)),
+               "pkv_bm_free_sequence")
+
+    def num_free(self) -> int:
+        return int(_lib.pkv_bm_num_free(self._sp()))
+
+    def refcount(self, block: int) -> int:
+        return int(_lib.pkv_bm_refcount(self._sp(), int(block)))
+
+    def block_hash(self, block: int) -> int:
+        return int(_lib.pkv_bm_block_hash(self._sp(), int(block)))
 
 
 def paged_gather(key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,

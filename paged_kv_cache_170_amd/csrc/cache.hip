@@ -1,4 +1,4 @@
-// Slot mapping, slot-mapped cache write and the paged gather diagnostic.
+// Slot mapping, slot-mapped cache write, block copy (copy-on-write) and the paged gather diagnostic.
 //
 // Slot mapping follows the block-table definition of "第2章:推理引擎核心技术" (aiinfra.vidrealm.tech)
 // §1.2 and the PagedAttention section of "Phase 17 · 04 — vLLM serving internals": the physical
@@ -68,6 +68,27 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
       *reinterpret_cast<uint16_t*>(value_pool + dst) = *reinterpret_cast<const uint16_t*>(vs);
     }
   }
+}
+
+// Block copy for copy-on-write ("第2章:推理引擎核心技术" §1.5): grid = (pieces / 256, num_pairs); each
+// thread moves one 16-byte piece of block src[i] to block dst[i] in both pools.  Blocks are
+// 16 * Hkv * hd * e bytes, a multiple of 16 * 64 * 2 = 2 KiB, so the pieces divide evenly.
+template <bool CHECK>
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ key_pool, char* __restrict__ value_pool,
+                                                          const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int64_t block_bytes,
+                                                          int num_blocks, int32_t* err_flag) {
+  const int i = blockIdx.y;
+  const int s = src[i], d = dst[i];
+  if (CHECK && (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err_flag, PKV_FLAG_BAD_BLOCK);
+    return;
+  }
+  if (s == d) return;
+  const int64_t off = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 16;
+  if (off >= block_bytes) return;
+  st16(key_pool + d * block_bytes + off, ld16(key_pool + s * block_bytes + off));
+  st16(value_pool + d * block_bytes + off, ld16(value_pool + s * block_bytes + off));
 }
 
 // Gather: grid = (ceil(max_len * pieces / 256), num_seqs); 16-byte pieces of whole token rows.
@@ -198,5 +219,28 @@ extern "C" pkv_status pkv_paged_gather(void* key_out, void* value_out, const voi
                        static_cast<char*>(value_out), static_cast<const char*>(key_pool),
                        static_cast<const char*>(value_pool), block_tables, max_blocks_per_seq, lengths, cu_out,
                        num_blocks, num_kv_heads, head_dim, e, err_flag);
+  return pkv_host::launch_status();
+}
+
+extern "C" pkv_status pkv_copy_blocks(void* key_pool, void* value_pool, const int32_t* src, const int32_t* dst,
+                                      int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, pkv_dtype dtype, int32_t* err_flag, void* stream) {
+  const int e = dtype_bytes(dtype);
+  if (e == 0 || block_size != kBlockSize || !head_dim_ok(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PKV_OK;
+  if (num_pairs > 65535) return PKV_ERR_UNSUPPORTED;  // grid y limit
+  if (!key_pool || !value_pool || !src || !dst) return PKV_ERR_INVALID_ARG;
+  for (const void* p : {static_cast<const void*>(key_pool), static_cast<const void*>(value_pool)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARG;
+  const int64_t block_bytes = static_cast<int64_t>(kBlockSize) * num_kv_heads * head_dim * e;
+  const dim3 grid(static_cast<unsigned>((block_bytes / 16 + 255) / 256), static_cast<unsigned>(num_pairs));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (err_flag)
+    hipLaunchKernelGGL(copy_blocks_kernel<true>, grid, dim3(256), 0, st, static_cast<char*>(key_pool),
+                       static_cast<char*>(value_pool), src, dst, block_bytes, num_blocks, err_flag);
+  else
+    hipLaunchKernelGGL(copy_blocks_kernel<false>, grid, dim3(256), 0, st, static_cast<char*>(key_pool),
+                       static_cast<char*>(value_pool), src, dst, block_bytes, num_blocks, err_flag);
   return pkv_host::launch_status();
 }

@@ -10,6 +10,7 @@ extern "C" const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, head ratio or block size";
     case PKV_ERR_WORKSPACE_TOO_SMALL: return "decode workspace too small";
     case PKV_ERR_HIP: return "HIP kernel launch failed";
+    case PKV_ERR_NO_SPACE: return "not enough free blocks";
   }
   return "unknown status";
 }

@@ -12,13 +12,14 @@ HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:pkv_status|size_t|int32_t|const char\*)\s+(pkv_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:pkv_status|size_t|int32_t|uint64_t|const char\*)\s+(pkv_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_calls():
     names = _declared()
     for must in ("pkv_cache_write", "pkv_paged_attn_decode", "pkv_paged_attn_prefill_chunk",
-                 "pkv_decode_workspace_bytes", "pkv_slot_mapping", "pkv_status_string"):
+                 "pkv_decode_workspace_bytes", "pkv_slot_mapping", "pkv_status_string", "pkv_copy_blocks",
+                 "pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free_sequence", "pkv_bm_block_hash"):
         assert must in names
 
 
@@ -36,6 +37,7 @@ def test_status_strings():
 
     assert pkv.status_string(0) == "ok"
     assert "workspace" in pkv.status_string(3)
+    assert "free blocks" in pkv.status_string(pkv.NO_SPACE)
     assert pkv.status_string(99) == "unknown status"
 
 

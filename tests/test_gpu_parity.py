@@ -471,3 +471,120 @@ def test_prefill_bf16_output_and_determinism(pkv, dev):
     diff = np.abs(ob - ref)
     assert (diff <= BF16_MAX_ABS + np.abs(ref) * 2.0 ** -8).all()
     assert int(err.item()) == 0
+
+
+# ------------------------------------------------------------------------------------------
+# Block manager + copy-on-write on the device
+# ------------------------------------------------------------------------------------------
+
+
+def _bf16_bits(rng, shape):
+    """N(0,1) drawn in fp32, rounded to bf16 (nearest even), as uint16 bit patterns."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_copy_blocks_bit_exact(pkv, dev):
+    _say("case copy_blocks: 300 of 1,000 bf16 blocks (8 x 128) copied, whole pools compared")
+    rng = np.random.default_rng(11)
+    nblk, hkv, hd = 1000, 8, 128
+    kp = _bf16_bits(rng, (nblk, 16, hkv, hd))
+    vp = _bf16_bits(rng, (nblk, 16, hkv, hd))
+    perm = rng.permutation(nblk).astype(np.int32)
+    src, dst = perm[:300].copy(), perm[300:600].copy()
+    src[:5] = dst[:5]  # src == dst: no-op
+    d_k, d_v = to_dev(kp, dev, "bf16"), to_dev(vp, dev, "bf16")
+    err = new_err(dev)
+    pkv.copy_blocks(d_k, d_v, to_dev(src, dev), to_dev(dst, dev), err_flag=err)
+    ek, ev = kp.copy(), vp.copy()
+    ek[dst] = kp[src]
+    ev[dst] = vp[src]
+    assert np.array_equal(to_host_storage(d_k, "bf16"), ek)
+    assert np.array_equal(to_host_storage(d_v, "bf16"), ev)
+    assert int(err.item()) == 0
+    # Checked mode: an out-of-range id is flagged and its pair skipped.
+    bad = torch.tensor([nblk + 3], dtype=torch.int32, device=dev)
+    pkv.copy_blocks(d_k, d_v, bad, to_dev(dst[:1], dev), err_flag=err)
+    assert int(err.item()) & pkv.FLAG_BAD_BLOCK
+    assert np.array_equal(to_host_storage(d_k, "bf16"), ek)
+
+
+def test_block_manager_prefix_cache_and_copy_on_write_decode(pkv, dev):
+    """Sequences built by the block manager: a shared system prompt (prefix-cache hits skip the
+    write of its full blocks), parallel samples forked from one request (their shared, partly
+    filled last block is copied on the first write), and a request freed before a new prompt
+    arrives.  Only the positions the manager reports as new are written; decode must then match the
+    oracle on each sequence's own logical K/V.  (Hits on freed blocks waiting in the free queue are
+    covered by the host-side tests.)"""
+    _say("case block manager: prefix cache + fork + copy-on-write -> decode, bf16 16/4 x 128")
+    rng = np.random.default_rng(12)
+    hq, hkv, hd, nblk, maxb = 16, 4, 128, 256, 32
+    bm = pkv.BlockManager(nblk, free_order=rng.permutation(nblk).astype(np.int32))
+    kp = torch.full((nblk, 16, hkv, hd), float("nan"), dtype=torch.bfloat16, device=dev)
+    vp = torch.full_like(kp, float("nan"))
+    err = new_err(dev)
+    sys_tok = rng.integers(0, 30000, 100)
+    sys_k, sys_v = _bf16_bits(rng, (100, hkv, hd)), _bf16_bits(rng, (100, hkv, hd))
+    seqs = []  # dict(row, ctx, tokens, k, v): k, v = the sequence's logical rows (bf16 bits)
+
+    def write(row, lo, hi, k, v, slots=None):
+        if hi <= lo:
+            return
+        if slots is None:
+            slots = np.array([row[p // 16] * 16 + p % 16 for p in range(lo, hi)], np.int32)
+        pkv.cache_write(to_dev(k[lo:hi], dev, "bf16"), to_dev(v[lo:hi], dev, "bf16"), kp, vp, to_dev(slots, dev),
+                        err_flag=err)
+
+    def add(tail_len):
+        tail = rng.integers(30000, 60000, tail_len)
+        toks = np.concatenate([sys_tok, tail])
+        k = np.concatenate([sys_k, _bf16_bits(rng, (tail_len, hkv, hd))])
+        v = np.concatenate([sys_v, _bf16_bits(rng, (tail_len, hkv, hd))])
+        row = np.full(maxb, -1, np.int32)
+        cached = bm.add_sequence(toks, row)
+        write(row, cached, len(toks), k, v)
+        seqs.append(dict(row=row, ctx=len(toks), k=k, v=v, cached=cached))
+
+    for n in (20, 150, 61, 3):
+        add(n)
+    assert seqs[0]["cached"] == 0 and all(s["cached"] == 96 for s in seqs[1:])
+    # Parallel samples of request 1: fork, then each appends its own tokens.
+    parent = seqs[1]
+    copies = 0
+    for n_new in (1, 17, 40):
+        row = np.full(maxb, -1, np.int32)
+        bm.fork(parent["row"], parent["ctx"], row)
+        slots, pairs = bm.append(row, parent["ctx"], n_new)
+        if len(pairs):
+            copies += 1
+            pkv.copy_blocks(kp, vp, to_dev(pairs[:, 0].copy(), dev), to_dev(pairs[:, 1].copy(), dev), err_flag=err)
+        k = np.concatenate([parent["k"], _bf16_bits(rng, (n_new, hkv, hd))])
+        v = np.concatenate([parent["v"], _bf16_bits(rng, (n_new, hkv, hd))])
+        write(row, parent["ctx"], parent["ctx"] + n_new, k, v, slots=slots)
+        seqs.append(dict(row=row, ctx=parent["ctx"] + n_new, k=k, v=v))
+    assert copies == 3  # request 1's last block (170 tokens) was shared and partly filled
+    # Free request 0; the next prompt still finds the system prompt's blocks.
+    first = seqs.pop(0)
+    bm.free_sequence(first["row"], first["ctx"])
+    add(45)
+    assert seqs[-1]["cached"] == 96
+    torch.cuda.synchronize()
+
+    B = len(seqs)
+    bt = np.stack([s["row"] for s in seqs])
+    ctx = np.array([s["ctx"] for s in seqs], np.int32)
+    q = _bf16_bits(rng, (B, hq, hd))
+    scale = 1.0 / math.sqrt(hd)
+    out = pkv.paged_attn_decode(to_dev(q, dev, "bf16"), kp, vp, to_dev(bt, dev), to_dev(ctx, dev), scale,
+                                err_flag=err)
+    ref = np.zeros((B, hq, hd))
+    qf = oracle.as_f64(q, "bf16")
+    for s in range(B):
+        K, V = oracle.as_f64(seqs[s]["k"], "bf16"), oracle.as_f64(seqs[s]["v"], "bf16")
+        for h in range(hq):
+            g = oracle.kv_head_of(h, hq, hkv)
+            ref[s, h] = oracle.softmax_attention(qf[s, h][None], K[:, g], V[:, g], scale, np.array([ctx[s]]))[0]
+    mx, mean = assert_close(out.cpu().numpy(), ref, "bf16", "block-manager decode")
+    _say(f"  {B} sequences, max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert int(err.item()) == 0
