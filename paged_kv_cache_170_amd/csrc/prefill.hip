@@ -47,7 +47,7 @@ struct PreCfg {
   static constexpr int KS = HD / 16;              // k-steps of S^T over head_dim
   static constexpr int MD = HD / 32;              // 32-row tiles of O^T
   static constexpr int KPITCH = HD * 2 + 16;      // LDS bytes per K row (conflict-free 16-byte reads)
-  static constexpr int VPITCH = HD * 2 + 32;      // LDS bytes per V row (conflict-free transposed reads)
+  static constexpr int VPITCH = HD * 2 + 64;      // LDS bytes per V row (transposed reads without bank conflicts)
   static constexpr int CPR = HD / 8;              // 16-byte chunks per row
   static constexpr int TILE = KT * (KPITCH + VPITCH);
   static constexpr int LOADS = 2 * KT * CPR / kPreThreads;  // chunks per thread per tensor per tile pair
