@@ -49,7 +49,10 @@ import numpy as np
 
 
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact fp64 value of stored elements: ``dtype`` "f32" (float32) or "bf16" (uint16 bit patterns)."""
+    """Exact fp64 value of stored elements: ``dtype`` "f32" (float32), "bf16" (uint16 bit patterns)
+    or "f64" (values already exact, e.g. a dequantised FP8 pool)."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -161,11 +164,13 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
 
 
 def decode(query: np.ndarray, key_pool: np.ndarray, value_pool: np.ndarray, block_tables: np.ndarray,
-           context_lens: np.ndarray, scale: float, dtype: str) -> np.ndarray:
+           context_lens: np.ndarray, scale: float, dtype: str, kv_dtype: str | None = None) -> np.ndarray:
     """One-token decode: ``out[s, h]`` is softmax attention of query ``(s, h)`` over the
     sequence's cached positions ``0 .. ctx_s-1`` of KV head ``kv_head_of(h)`` ([Chunked-Prefill]:
     decode reads the whole cache each step; [Engine-core] §1.4: the paged kernel walks the
-    request's pages through the table)."""
+    request's pages through the table).  ``kv_dtype`` is the pools' storage type when it differs
+    from the query's."""
+    kv_dtype = kv_dtype or dtype
     B, hq, hd = query.shape
     hkv = key_pool.shape[2]
     q = as_f64(query, dtype)
@@ -174,8 +179,8 @@ def decode(query: np.ndarray, key_pool: np.ndarray, value_pool: np.ndarray, bloc
         n = int(context_lens[s])
         if n == 0:
             continue
-        K = as_f64(gather(key_pool, block_tables[s], n), dtype)
-        V = as_f64(gather(value_pool, block_tables[s], n), dtype)
+        K = as_f64(gather(key_pool, block_tables[s], n), kv_dtype)
+        V = as_f64(gather(value_pool, block_tables[s], n), kv_dtype)
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             out[s, h] = softmax_attention(q[s, h][None, :], K[:, g], V[:, g], scale, np.array([n]))[0]
@@ -184,14 +189,16 @@ def decode(query: np.ndarray, key_pool: np.ndarray, value_pool: np.ndarray, bloc
 
 def prefill_chunk(query: np.ndarray, cu_q_lens: np.ndarray, chunk_offsets: np.ndarray, key_pool: np.ndarray,
                   value_pool: np.ndarray, block_tables: np.ndarray, scale: float, dtype: str,
-                  causal: bool = True, rows=None) -> np.ndarray:
+                  causal: bool = True, rows=None, kv_dtype: str | None = None) -> np.ndarray:
     """Chunked-prefill attention ([Chunked-Prefill], section on how chunked prefill works).
 
     Sequence ``s`` has chunk rows ``cu_q_lens[s] .. cu_q_lens[s+1]-1`` at absolute positions
     ``chunk_offsets[s] + i``; its cache already holds positions ``0 .. offset+L-1`` (earlier
     chunks plus this chunk).  Row ``i`` attends to ``visible_keys(i, ...)`` keys.  ``rows``
     optionally restricts the computation to a subset of packed row indices (others stay zero).
+    ``kv_dtype`` is the pools' storage type when it differs from the query's.
     """
+    kv_dtype = kv_dtype or dtype
     total, hq, hd = query.shape
     hkv = key_pool.shape[2]
     out = np.zeros((total, hq, hd), dtype=np.float64)
@@ -205,8 +212,8 @@ def prefill_chunk(query: np.ndarray, cu_q_lens: np.ndarray, chunk_offsets: np.nd
         idx = [i for i in range(L) if want is None or (lo + i) in want]
         if not idx:
             continue
-        K = as_f64(gather(key_pool, block_tables[s], o + L), dtype)
-        V = as_f64(gather(value_pool, block_tables[s], o + L), dtype)
+        K = as_f64(gather(key_pool, block_tables[s], o + L), kv_dtype)
+        V = as_f64(gather(value_pool, block_tables[s], o + L), kv_dtype)
         q = as_f64(query[lo:hi][idx], dtype)
         vis = np.array([visible_keys(i, o, L, causal) for i in idx])
         for h in range(hq):
