@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixed_step", choices=["mixed_step", "gqa_decode", "long_decode"])
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="KV pool storage: bf16, or E4M3 codes with per-pool scales (quantised from the bf16 "
+                         "pools at setup; the step's new tokens go through the quantising write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra untimed-for-value steps, each after a 1 GiB write that flushes L2 and MALL")
@@ -74,7 +77,7 @@ def counter_traffic(kernel_key: str, src: str):
 
 
 def unique_kv_bytes(case) -> int:
-    """K+V bytes of the distinct pool rows the decode reads (shared blocks counted once)."""
+    """K+V elements of the distinct pool rows the decode reads (shared blocks counted once)."""
     rows = set()
     for s in range(case.num_seqs):
         n = int(case.context_lens[s])
@@ -83,12 +86,13 @@ def unique_kv_bytes(case) -> int:
             b = int(case.block_tables[s, j])
             cnt = 16 if j < nb - 1 else n - 16 * (nb - 1)
             rows.update(b * 16 + o for o in range(cnt))
-    return len(rows) * 2 * case.num_kv_heads * case.head_dim * case.elem_bytes
+    return len(rows) * 2 * case.num_kv_heads * case.head_dim
 
 
-def decode_algorithmic_bytes(case, out_bytes=4):
-    kv = unique_kv_bytes(case)
-    logical = int(case.context_lens.astype(np.int64).sum()) * 2 * case.num_kv_heads * case.head_dim * case.elem_bytes
+def decode_algorithmic_bytes(case, out_bytes=4, kv_elem=None):
+    kv_elem = case.elem_bytes if kv_elem is None else kv_elem
+    kv = unique_kv_bytes(case) * kv_elem
+    logical = int(case.context_lens.astype(np.int64).sum()) * 2 * case.num_kv_heads * case.head_dim * kv_elem
     q = case.num_seqs * case.num_q_heads * case.head_dim * case.elem_bytes
     o = case.num_seqs * case.num_q_heads * case.head_dim * out_bytes
     table = 4 * int(sum(-(-int(n) // 16) for n in case.context_lens))
@@ -155,6 +159,21 @@ def main():
         w_k, w_v = to_dev(wcase.key_new, bf), to_dev(wcase.value_new, bf)
         w_max = int(np.diff(wcase.new_cu_lens).max())
         slots = torch.empty(wcase.num_new_tokens, dtype=torch.int32, device=dev)
+    fp8 = args.kv == "fp8"
+    if fp8 and not bf:
+        raise SystemExit("--kv fp8 needs a bf16 workload")
+    # FP8 pools: every slot of the bf16 pools quantised by the library's own write (setup, untimed).
+    # Scale 2^-5 for both pools: N(0,1) values stay far inside E4M3's +-448 range.
+    k_scale = v_scale = 2.0 ** -5
+    if fp8:
+        kp8 = torch.empty(kp.shape, dtype=torch.float8_e4m3fn, device=dev)
+        vp8 = torch.empty_like(kp8)
+        nrow = kp.shape[0] * kp.shape[1]
+        all_slots = torch.arange(nrow, dtype=torch.int32, device=dev)
+        pkv.cache_write_fp8(kp.view(nrow, kp.shape[2], kp.shape[3]), vp.view(nrow, vp.shape[2], vp.shape[3]), kp8, vp8,
+                            all_slots, k_scale, v_scale)
+        torch.cuda.synchronize()
+        del all_slots
     d_q = to_dev(dec.query, bf)
     d_bt, d_ctx = to_dev(dec.block_tables), to_dev(dec.context_lens)
     d_out = torch.empty((dec.num_seqs, dec.num_q_heads, dec.head_dim), dtype=torch.float32, device=dev)
@@ -189,12 +208,23 @@ def main():
             pkv.slot_mapping(w_bt, w_cu, w_start, w_max, dec.num_blocks, out=slots)
         mark(1)
         if has_write:
-            pkv.cache_write(w_k, w_v, kp, vp, slots)
+            if fp8:
+                pkv.cache_write_fp8(w_k, w_v, kp8, vp8, slots, k_scale, v_scale)
+            else:
+                pkv.cache_write(w_k, w_v, kp, vp, slots)
         mark(2)
-        pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=d_out, workspace=ws)
+        if fp8:
+            pkv.paged_attn_decode_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, out=d_out, workspace=ws)
+        else:
+            pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=d_out, workspace=ws)
         mark(3)
         if pre is not None:
-            pkv.paged_attn_prefill_chunk(p_q, p_cu, p_off, kp, vp, p_bt, p_maxl, pre.scale, causal=True, out=p_out)
+            if fp8:
+                pkv.paged_attn_prefill_chunk_fp8(p_q, p_cu, p_off, kp8, vp8, p_bt, p_maxl, pre.scale, k_scale, v_scale,
+                                                 causal=True, out=p_out)
+            else:
+                pkv.paged_attn_prefill_chunk(p_q, p_cu, p_off, kp, vp, p_bt, p_maxl, pre.scale, causal=True,
+                                             out=p_out)
         mark(4)
 
     for _ in range(args.warmup):
@@ -280,7 +310,7 @@ def main():
     bm_us = (time.perf_counter() - t_bm) * 1e6 / (3 * dec.num_seqs)
     bm_info = {"sequences": dec.num_seqs, "prefix_hits": hits, "us_per_operation": bm_us}
 
-    dec_bytes, dec_kv_unique, dec_kv_logical = decode_algorithmic_bytes(dec)
+    dec_bytes, dec_kv_unique, dec_kv_logical = decode_algorithmic_bytes(dec, kv_elem=1 if fp8 else None)
     dec_s = avg_ms["decode"] * 1e-3
     dec_gbs = dec_bytes / dec_s / 1e9
     secondary = {
@@ -310,28 +340,34 @@ def main():
             secondary["prefill_tflops_cold"] = fl / (float(np.median(cold["prefill"])) * 1e-3) / 1e12
         kernels["prefill"] = (avg_ms["prefill"], "mfma", fl, pre_tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s", "prefill.hip")
     if has_write:
-        wb = 2 * wcase.num_new_tokens * wcase.num_kv_heads * wcase.head_dim * wcase.elem_bytes * 2 + 4 * wcase.num_new_tokens
+        # read the new rows (bf16 or fp32) and write them into the pools (E4M3: one byte each)
+        wb = (2 * wcase.num_new_tokens * wcase.num_kv_heads * wcase.head_dim * (wcase.elem_bytes + (1 if fp8 else wcase.elem_bytes))
+              + 4 * wcase.num_new_tokens)
         secondary.update({"cache_write_ms": avg_ms["cache_write"], "slot_mapping_ms": avg_ms["slot_mapping"],
                           "cache_write_gbs": wb / (avg_ms["cache_write"] * 1e-3) / 1e9})
     dominant = max(kernels, key=lambda k: kernels[k][0])
     ms, bound, work, achieved, peak, unit, src = kernels[dominant]
+    tag = args.workload + ("_fp8" if fp8 else "")
     roofline = {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
-                "frac": achieved / peak, "traffic": counter_traffic(f"{dominant}_{args.workload}", src),
+                "frac": achieved / peak, "traffic": counter_traffic(f"{dominant}_{tag}", src),
                 "work_per_launch": work, "avg_launch_ms": ms}
     for k, (ms_k, bound_k, work_k, ach_k, peak_k, unit_k, src_k) in kernels.items():
         secondary[f"roofline_{k}"] = {"bound": bound_k, "achieved": ach_k, "peak": peak_k, "unit": unit_k,
                                       "frac": ach_k / peak_k,
-                                      "traffic": counter_traffic(f"{k}_{args.workload}", src_k)}
+                                      "traffic": counter_traffic(f"{k}_{tag}", src_k)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if fp8:
+        print("[bench] cpu baseline is reported for the bf16 pools only", file=sys.stderr, flush=True)
+    elif not args.no_cpu_baseline:
         cpu = cpu_baseline(dec, pre, kp, vp, has_write, args, torch)
 
     config = {"workload": args.workload, "num_seqs_decode": dec.num_seqs, "q_heads": dec.num_q_heads,
               "kv_heads": dec.num_kv_heads, "head_dim": dec.head_dim, "block_size": 16,
               "context_lens": "uniform 200..8192, shared 63-block prefix" if args.workload == "mixed_step" else
               ("lognormal mean 1500, sd 600, clipped 16..8192" if args.workload == "gqa_decode" else "4096 each"),
-              "seed": {"mixed_step": 5, "gqa_decode": 3, "long_decode": 4}[args.workload]}
+              "seed": {"mixed_step": 5, "gqa_decode": 3, "long_decode": 4}[args.workload],
+              "kv_storage": "fp8_e4m3 (k_scale = v_scale = 2^-5)" if fp8 else ("bf16" if bf else "f32")}
     if pre is not None:
         config.update({"prefill_chunk": int(pre.cu_q_lens[-1]), "prefill_offset": int(pre.chunk_offsets[0])})
     line = {"metric": "paged decode KV-read GB/s (% HBM peak); chunked-prefill TFLOP/s (% MFMA)",

@@ -74,7 +74,10 @@ typedef enum {
   PKV_ERR_NO_SPACE = 5             /* block manager: not enough free blocks (state left unchanged) */
 } pkv_status;
 
-typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1 } pkv_dtype;
+/* Element types.  FP8_E4M3 is the OCP 8-bit floating point E4M3 encoding (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, largest finite 448); it is only
+ * a pool storage type, used with a per-pool fp32 scale by the *_fp8 calls below. */
+typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1, PKV_DTYPE_FP8_E4M3 = 2 } pkv_dtype;
 
 /* Bits OR-ed into *err_flag by checked kernels. */
 #define PKV_FLAG_BAD_BLOCK 1   /* a block-table entry the call had to read is outside [0, num_blocks) */
@@ -123,7 +126,8 @@ pkv_status pkv_cache_write(const void* key, const void* value, int64_t key_tok_s
  * Copies sequence s's first lengths[s] token rows of both pools, in logical order, into
  * key_out / value_out rows cu_out[s] .. cu_out[s] + lengths[s] - 1, bit for bit, using the same
  * address arithmetic as the attention kernels.  A diagnostic used to test block indexing.
- *   key_out, value_out  [cu_out[num_seqs], num_kv_heads, head_dim], pool dtype
+ *   key_out, value_out  [cu_out[num_seqs], num_kv_heads, head_dim], pool dtype (F32, BF16 or
+ *                       FP8_E4M3; a bit copy in every case)
  *   lengths, cu_out     int32 [num_seqs] and [num_seqs + 1] (device)
  *   max_len             host upper bound of lengths[s] (sizes the grid)
  */
@@ -196,11 +200,59 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
                                         pkv_dtype dtype, int32_t* err_flag, void* stream);
 
 /*
+ * FP8 KV pool.  The pages run their model in FP8 ([vLLM-internals], opening benchmark and memory
+ * section) without saying how a cache would be stored in it; these calls keep K and V pools of
+ * E4M3 codes, one fp32 scale per pool (k_scale, v_scale > 0, finite), so that a code c stands for
+ * value(c) * scale.  Pools are [num_blocks, 16, num_kv_heads, head_dim] bytes, token-major as for
+ * the other dtypes; slot mapping, block tables, the gather and the block copy are unchanged.
+ *
+ * Cache write with quantisation: for t < num_tokens with slot = slot_mapping[t] >= 0, every
+ * element x of key row t (bf16 or fp32 as in_dtype, widened exactly to fp32) is stored as the
+ * E4M3 code of the fp32 product x * (1 / k_scale), the reciprocal rounded to nearest in fp32;
+ * the product rounds to the nearest E4M3 value with ties to the even code, magnitudes >= 448 and
+ * infinities saturate to +-448, NaN becomes the NaN code 0x7F, the sign of zero is kept.  Value
+ * rows alike with v_scale.  Negative slots are skipped; duplicate slots are a caller error.
+ *   key, value   [num_tokens, num_kv_heads, head_dim], token strides in elements
+ *   key_pool, value_pool  FP8_E4M3 pools (16-byte aligned)
+ */
+pkv_status pkv_cache_write_fp8(const void* key, const void* value, int64_t key_tok_stride, int64_t value_tok_stride,
+                               void* key_pool, void* value_pool, const int32_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               pkv_dtype in_dtype, float k_scale, float v_scale, int32_t* err_flag, void* stream);
+
+/*
+ * Decode over FP8 pools ([Chunked-Prefill] section on prefill and decode; [Engine-core] §1.4):
+ * pkv_paged_attn_decode with K_s[j] and V_s[j] replaced by their dequantised
+ * values value(code) * k_scale and value(code) * v_scale.  query is bf16; out F32 or BF16.  The
+ * workspace and split_tokens rules are those of pkv_paged_attn_decode (same sizes).
+ */
+pkv_status pkv_paged_attn_decode_fp8(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                     const void* value_pool, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t num_blocks, float scale, float k_scale, float v_scale,
+                                     int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                     int32_t* err_flag, void* stream);
+
+/*
+ * Chunked prefill over FP8 pools ([Chunked-Prefill], section on how chunked prefill works):
+ * pkv_paged_attn_prefill_chunk with dequantised K and V as above; query bf16, out F32 or BF16.
+ */
+pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_dtype, const void* query,
+                                            const int32_t* cu_q_lens, const int32_t* chunk_offsets,
+                                            const void* key_pool, const void* value_pool,
+                                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                            int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                            int32_t causal, float scale, float k_scale, float v_scale,
+                                            int32_t* err_flag, void* stream);
+
+/*
  * Block copy for copy-on-write ([Engine-core] §1.5; [C13-L2] 改进二, sharing paragraph): for each
  * pair i, the whole block src[i] (16 rows x num_kv_heads x head_dim, K and V) is copied bit for bit
  * to block dst[i].  src / dst: int32 [num_pairs] device arrays; src[i] == dst[i] is a no-op; a
  * block that is a destination must not be a source or destination of another pair in the same call
- * (undefined otherwise).  dtype F32 or BF16 (a bit copy either way).  With err_flag, ids outside
+ * (undefined otherwise).  dtype F32, BF16 or FP8_E4M3 (a bit copy in every case).  With err_flag, ids outside
  * [0, num_blocks) set PKV_FLAG_BAD_BLOCK and that pair is skipped.
  */
 pkv_status pkv_copy_blocks(void* key_pool, void* value_pool, const int32_t* src, const int32_t* dst,

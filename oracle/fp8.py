@@ -56,28 +56,21 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
-    """Nearest E4M3 code of each value, ties to the even code, saturating at 448; NaN -> NaN."""
+    """Nearest E4M3 code of each value, ties to the even code, saturating at 448; NaN -> NaN.
+
+    For each magnitude, the two neighbouring entries of the table of finite magnitudes are found
+    by binary search and the closer one is taken (the even code on a tie)."""
     v = np.asarray(v, dtype=np.float64)
-    out = np.empty(v.shape, dtype=np.uint8)
-    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
-    for i, x in enumerate(flat_v):
-        if np.isnan(x):
-            flat_o[i] = NAN_CODE
-            continue
-        sign = 0x80 if np.signbit(x) else 0
-        a = abs(x)
-        if a >= E4M3_MAX:
-            flat_o[i] = sign | 0x7E
-            continue
-        hi = int(np.searchsorted(_POS, a, side="left"))  # first magnitude >= a
-        if _POS[hi] == a:
-            c = hi
-        else:
-            lo = hi - 1
-            dlo, dhi = a - _POS[lo], _POS[hi] - a
-            c = lo if dlo < dhi else hi if dhi < dlo else (lo if lo % 2 == 0 else hi)
-        flat_o[i] = sign | c
-    return out
+    a = np.abs(v)
+    nan = np.isnan(v)
+    a_safe = np.where(nan, 0.0, np.minimum(a, E4M3_MAX))
+    hi = np.searchsorted(_POS, a_safe, side="left")          # first magnitude >= a (<= 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a_safe - _POS[lo], _POS[hi] - a_safe
+    pick_lo = (dlo < dhi) | ((dlo == dhi) & (lo % 2 == 0))
+    code = np.where(_POS[hi] == a_safe, hi, np.where(pick_lo, lo, hi)).astype(np.uint8)
+    code = code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    return np.where(nan, np.uint8(NAN_CODE), code).astype(np.uint8)
 
 
 def reciprocal_f32(scale: float) -> np.float32:
@@ -88,8 +81,16 @@ def reciprocal_f32(scale: float) -> np.float32:
 def quantize(x_f32: np.ndarray, scale: float) -> np.ndarray:
     """Codes of fp32 elements for a pool with this scale: product with the fp32 reciprocal, taken
     in fp32, then rounded to E4M3."""
-    prod = np.asarray(x_f32, dtype=np.float32) * reciprocal_f32(scale)  # one IEEE fp32 multiply each
+    with np.errstate(over="ignore", invalid="ignore"):  # overflow to inf saturates; NaN stays NaN
+        prod = np.asarray(x_f32, dtype=np.float32) * reciprocal_f32(scale)  # one IEEE fp32 multiply each
     return e4m3_encode(prod.astype(np.float64))
+
+
+def quantize_bf16_bits(bits: np.ndarray, scale: float) -> np.ndarray:
+    """quantize() of bf16 elements given as uint16 bit patterns, evaluated once for each of the
+    65,536 patterns and looked up (the same function, cheaper on large pools)."""
+    every = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    return quantize(every, scale)[np.asarray(bits, dtype=np.uint16)]
 
 
 def cache_write_fp8(key_pool: np.ndarray, value_pool: np.ndarray, key_f32: np.ndarray, value_f32: np.ndarray,

@@ -8,7 +8,9 @@ loudly (there is no fallback).
 
 Tensors: pools are ``[num_blocks, 16, num_kv_heads, head_dim]`` (K and V
 separate, same dtype); block tables, context lengths, slot mappings and
-offsets are int32 device tensors.
+offsets are int32 device tensors.  FP8 pools hold E4M3 codes as
+``torch.float8_e4m3fn`` (or ``torch.uint8``) tensors and come with one fp32
+scale per pool (the ``*_fp8`` calls).
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, NO_SPACE = 0, 1, 2, 3, 4, 5
-DTYPE_F32, DTYPE_BF16 = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 FLAG_BAD_BLOCK, FLAG_BAD_SLOT, FLAG_BAD_LENGTH = 1, 2, 4
 BLOCK_SIZE = 16
 
@@ -44,6 +46,12 @@ _SIGS = {
                                      _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
+    "pkv_cache_write_fp8": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                   _f32, _vp, _vp]),
+    "pkv_paged_attn_decode_fp8": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_paged_attn_prefill_chunk_fp8": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _vp]),
     "pkv_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_bm_state_bytes": (_sz, [_i32]),
@@ -84,7 +92,15 @@ def _dtype_code(t: torch.Tensor) -> int:
         return DTYPE_F32
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return DTYPE_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_fp8_pools(key_pool: torch.Tensor, value_pool: torch.Tensor):
+    if _dtype_code(key_pool) != DTYPE_FP8_E4M3:
+        raise ValueError("FP8 pools must be float8_e4m3fn (or uint8 code) tensors")
+    return _pool_dims(key_pool, value_pool)
 
 
 def _ptr(t):
@@ -150,6 +166,30 @@ def cache_write(key: torch.Tensor, value: torch.Tensor, key_pool: torch.Tensor, 
     _check(_lib.pkv_cache_write(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_pool),
                                 _ptr(value_pool), _ptr(slot_mapping), T, nblk, hkv, hd, bs,
                                 _dtype_code(key_pool), _ptr(err_flag), _stream(key.device)), "pkv_cache_write")
+
+
+def cache_write_fp8(key: torch.Tensor, value: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                    slot_mapping: torch.Tensor, k_scale: float, v_scale: float,
+                    err_flag: torch.Tensor | None = None) -> None:
+    """Quantise token rows key[t], value[t] (bf16 or fp32) into E4M3 pool slots slot_mapping[t];
+    see pkv_cache_write_fp8."""
+    _need_gpu(key, value, key_pool, value_pool, slot_mapping, err_flag)
+    _need_i32(slot_mapping, err_flag)
+    nblk, bs, hkv, hd = _need_fp8_pools(key_pool, value_pool)
+    for t in (key, value):
+        if t.dtype not in (torch.float32, torch.bfloat16) or t.dim() != 3 or tuple(t.shape[1:]) != (hkv, hd):
+            raise ValueError("key/value must be [T, num_kv_heads, head_dim] in bf16 or fp32")
+        if t.stride(2) != 1 or t.stride(1) != hd:
+            raise ValueError("key/value rows must be contiguous")
+    if key.dtype != value.dtype:
+        raise ValueError("key and value must have the same dtype")
+    T = key.shape[0]
+    if value.shape[0] != T or slot_mapping.shape[0] < T:
+        raise ValueError("token counts differ")
+    _check(_lib.pkv_cache_write_fp8(_ptr(key), _ptr(value), key.stride(0), value.stride(0), _ptr(key_pool),
+                                    _ptr(value_pool), _ptr(slot_mapping), T, nblk, hkv, hd, bs, _dtype_code(key),
+                                    float(k_scale), float(v_scale), _ptr(err_flag), _stream(key.device)),
+           "pkv_cache_write_fp8")
 
 
 def copy_blocks(key_pool: torch.Tensor, value_pool: torch.Tensor, src: torch.Tensor, dst: torch.Tensor,
@@ -296,6 +336,35 @@ def paged_attn_decode(query: torch.Tensor, key_pool: torch.Tensor, value_pool: t
     return out
 
 
+def paged_attn_decode_fp8(query: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, k_scale: float,
+                          v_scale: float, out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                          workspace: torch.Tensor | None = None, split_tokens: int = 0,
+                          err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """One-token decode over E4M3 pools with per-pool scales; see pkv_paged_attn_decode_fp8."""
+    _need_gpu(query, key_pool, value_pool, block_tables, context_lens, out, workspace, err_flag)
+    _need_i32(block_tables, context_lens, err_flag)
+    nblk, bs, hkv, hd = _need_fp8_pools(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != torch.bfloat16 or not query.is_contiguous():
+        raise ValueError("query must be contiguous bf16 [num_seqs, num_q_heads, head_dim]")
+    B, hq, _ = query.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((B, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (B, hq, hd):
+        raise ValueError("out must be contiguous [num_seqs, num_q_heads, head_dim]")
+    if workspace is None:
+        workspace = decode_workspace(query, hkv, block_tables.shape[1], split_tokens)
+    _check(_lib.pkv_paged_attn_decode_fp8(_ptr(out), _dtype_code(out), _ptr(query), _ptr(key_pool),
+                                          _ptr(value_pool), _ptr(block_tables), block_tables.shape[1],
+                                          _ptr(context_lens), B, hq, hkv, hd, nblk, float(scale), float(k_scale),
+                                          float(v_scale), int(split_tokens), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _ptr(err_flag),
+                                          _stream(query.device)), "pkv_paged_attn_decode_fp8")
+    return out
+
+
 def paged_attn_prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk_offsets: torch.Tensor,
                              key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,
                              max_q_len: int, scale: float, causal: bool = True, out: torch.Tensor | None = None,
@@ -321,6 +390,35 @@ def paged_attn_prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk
                                              hkv, hd, nblk, int(bool(causal)), float(scale), _dtype_code(key_pool),
                                              _ptr(err_flag), _stream(query.device)),
            "pkv_paged_attn_prefill_chunk")
+    return out
+
+
+def paged_attn_prefill_chunk_fp8(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk_offsets: torch.Tensor,
+                                 key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,
+                                 max_q_len: int, scale: float, k_scale: float, v_scale: float, causal: bool = True,
+                                 out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                                 err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunked-prefill attention over E4M3 pools with per-pool scales; see
+    pkv_paged_attn_prefill_chunk_fp8."""
+    _need_gpu(query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables, out, err_flag)
+    _need_i32(cu_q_lens, chunk_offsets, block_tables, err_flag)
+    nblk, bs, hkv, hd = _need_fp8_pools(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != torch.bfloat16 or not query.is_contiguous():
+        raise ValueError("query must be contiguous bf16 [rows, num_q_heads, head_dim]")
+    rows, hq, _ = query.shape
+    num_seqs = chunk_offsets.shape[0]
+    if cu_q_lens.shape[0] != num_seqs + 1 or block_tables.shape[0] != num_seqs:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((rows, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (rows, hq, hd):
+        raise ValueError("out must be contiguous [rows, num_q_heads, head_dim]")
+    _check(_lib.pkv_paged_attn_prefill_chunk_fp8(_ptr(out), _dtype_code(out), _ptr(query), _ptr(cu_q_lens),
+                                                 _ptr(chunk_offsets), _ptr(key_pool), _ptr(value_pool),
+                                                 _ptr(block_tables), block_tables.shape[1], num_seqs,
+                                                 int(max_q_len), hq, hkv, hd, nblk, int(bool(causal)), float(scale),
+                                                 float(k_scale), float(v_scale), _ptr(err_flag),
+                                                 _stream(query.device)), "pkv_paged_attn_prefill_chunk_fp8")
     return out
 
 

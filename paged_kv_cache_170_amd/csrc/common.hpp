@@ -77,6 +77,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sixteen E4M3 codes (one 16-byte load, element i in byte i) to sixteen bf16 values in the same
+// order.  Exact: every E4M3 value is a bf16 value (the conversion's scale operand is 1).
+__device__ __forceinline__ void e4m3x16_to_bf16(uint4 c, uint4& lo, uint4& hi) {
+#define PKV_CV(W, H) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(W, 1.0f, H))
+  lo = uint4{PKV_CV(c.x, false), PKV_CV(c.x, true), PKV_CV(c.y, false), PKV_CV(c.y, true)};
+  hi = uint4{PKV_CV(c.z, false), PKV_CV(c.z, true), PKV_CV(c.w, false), PKV_CV(c.w, true)};
+#undef PKV_CV
+}
+
 // LDS transpose read of four 16-bit elements.  Within each group of 16 lanes, lane i receives
 // element (i % 4) of the 8-byte rows addressed by lanes 4e + i/4 (e = 0..3) of its group.
 // `lds_ptr` must point into __shared__ memory and be 8-byte aligned.

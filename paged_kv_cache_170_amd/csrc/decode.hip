@@ -33,13 +33,15 @@ constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kMaxGroup = 16;
 constexpr float kMaxWeight = 1048576.f;  // 2^20: largest softmax weight before the reference max moves
 
-template <int HD>
+// E: bytes per pool element (2 for bf16, 1 for E4M3 codes); staging in LDS is bf16 either way.
+template <int HD, int E = 2>
 struct DecCfg {
   static constexpr int KK = HD / 32;          // k-steps of S^T = K Q^T over head_dim
   static constexpr int MT = HD / 16;          // 16-row tiles of O^T
   static constexpr int KPITCH = HD * 2 + 16;  // bytes per staged K row (conflict-free 16-byte reads)
   static constexpr int VPITCH = HD * 2 + 32;  // bytes per staged V row (conflict-free transposed reads)
-  static constexpr int LPR = HD / 8;          // lanes per row in a 16-byte-per-lane load
+  static constexpr int EPL = 16 / E;          // pool elements per 16-byte lane load
+  static constexpr int LPR = HD / EPL;        // lanes per row in a 16-byte-per-lane load
   static constexpr int RPL = kWave / LPR;     // rows per wave-wide load
   static constexpr int VLD = kBlockSize / RPL;  // wave-wide loads per block and tensor
   static constexpr int STAGE = 2 * kBlockSize * (KPITCH + VPITCH);  // bytes per wave (two blocks of K and V)
@@ -59,7 +61,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool 
 template <int HD>
 __device__ __forceinline__ void merge_waves(const float* comb_o, const float* comb_ml, int group, int s, int g,
                                             int split, int nsplit, int max_splits, int num_q_heads, float* ws_o,
-                                            float* ws_ml, void* out, bool out_bf16) {
+                                            float* ws_ml, void* out, bool out_bf16, float v_scale) {
   for (int i = threadIdx.x; i < group * HD; i += kDecThreads) {
     const int hn = i / HD, d = i - hn * HD;
     float M = -INFINITY;
@@ -75,6 +77,8 @@ __device__ __forceinline__ void merge_waves(const float* comb_o, const float* co
     }
     const int h = g * group + hn;
     const int64_t row = static_cast<int64_t>(s) * num_q_heads + h;
+    // v_scale: the FP8 pool's V scale (1 for bf16 pools, where the product is exact).
+    O *= v_scale;
     if (nsplit == 1) {
       store_out(out, row * HD + d, L > 0.f ? O / L : 0.f, out_bf16);
     } else {
@@ -101,8 +105,8 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int32_t* err_f
 // Kernel arguments of the bf16 decode (one struct so that every launch form shares them).
 struct DecArgs {
   const uint16_t* query;
-  const uint16_t* key_pool;
-  const uint16_t* value_pool;
+  const void* key_pool;    // bf16 or E4M3 codes
+  const void* value_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
   float* ws_o;
@@ -110,13 +114,14 @@ struct DecArgs {
   void* out;
   int32_t* err_flag;
   int max_blocks, num_q_heads, num_kv_heads, group, num_blocks, split_tokens, max_splits, out_bf16;
-  float scale_log2;
+  float scale_log2;  // scale * log2(e), times the K scale for FP8 pools
+  float v_scale;     // V scale of an FP8 pool, 1 for bf16
 };
 
-template <int HD>
+template <int HD, int E>
 struct DecBuf {
-  uint4 k[2][DecCfg<HD>::VLD];
-  uint4 v[2][DecCfg<HD>::VLD];
+  uint4 k[2][DecCfg<HD, E>::VLD];
+  uint4 v[2][DecCfg<HD, E>::VLD];
   int b0, b1;
 };
 
@@ -152,14 +157,15 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   for (int kk = 0; kk < DecCfg<HD>::KK; ++kk) it.qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
 }
 
-template <int HD, bool CHECK, bool NARROW>
+template <int HD, bool CHECK, bool NARROW, bool KV8>
 __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecItem<HD>& it, char* smem) {
-  using C = DecCfg<HD>;
+  constexpr int E = KV8 ? 1 : 2;  // pool bytes per element
+  using C = DecCfg<HD, E>;
   const int s = it.s, g = it.g, split = it.split, ctx = it.ctx, nsplit = it.nsplit;
   const int my_id0 = it.my_id[0], my_id1 = it.my_id[1];
   const bf16x8* qf = it.qf;
-  const uint16_t* __restrict__ key_pool = A_.key_pool;
-  const uint16_t* __restrict__ value_pool = A_.value_pool;
+  const void* __restrict__ key_pool = A_.key_pool;
+  const void* __restrict__ value_pool = A_.value_pool;
   const int num_q_heads = A_.num_q_heads, num_kv_heads = A_.num_kv_heads, group = A_.group;
   const int num_blocks = A_.num_blocks, split_tokens = A_.split_tokens;
   const float scale_log2 = A_.scale_log2;
@@ -178,14 +184,14 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   char* kstage = smem + wave * C::STAGE;                      // [32 rows][KPITCH]
   char* vstage = kstage + 2 * kBlockSize * C::KPITCH;         // [32 rows][VPITCH]
   const int units = (tok_end - tok0 + 31) / 32;
-  const int row_base = lane / C::LPR, col = (lane % C::LPR) * 8;
+  const int row_base = lane / C::LPR, col = (lane % C::LPR) * C::EPL;  // col: first element of the lane
 
   // Step u covers positions tok0 + 32u .. +31 (two blocks).  K and V rows are read whole (each
   // wave-wide load covers RPL complete rows) and staged in LDS in their natural layout.
-  const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * 2);
-  const uint32_t row_bytes = static_cast<uint32_t>(num_kv_heads * HD * 2);
-  const uint32_t c0 = static_cast<uint32_t>((row_base * num_kv_heads + g) * HD * 2 + col * 2);
-  auto load = [&](int u, DecBuf<HD>& B) {
+  const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * E);
+  const uint32_t row_bytes = static_cast<uint32_t>(num_kv_heads * HD * E);
+  const uint32_t c0 = static_cast<uint32_t>((row_base * num_kv_heads + g) * HD * E + col * E);
+  auto load = [&](int u, DecBuf<HD, E>& B) {
     const int t0 = tok0 + 32 * u;
     // Blocks 2u and 2u + 1 of the split (u is the same across the wave).
     const int idreg = u < kWave / 2 ? my_id0 : my_id1;
@@ -209,16 +215,28 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
     }
   };
 
-  auto compute = [&](int u, const DecBuf<HD>& B) {
+  auto compute = [&](int u, const DecBuf<HD, E>& B) {
     const int t0 = tok0 + 32 * u;
-    // Stage K and V (V rows at or past ctx become zero so stale slots never reach the MFMA).
+    // Stage K and V as bf16 (V rows at or past ctx become zero so stale slots never reach the
+    // MFMA).  E4M3 codes are converted exactly on the way.
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
 #pragma unroll
       for (int i = 0; i < C::VLD; ++i) {
         const int row = pg * kBlockSize + i * C::RPL + row_base;
-        st16(kstage + row * C::KPITCH + col * 2, B.k[pg][i]);
-        st16(vstage + row * C::VPITCH + col * 2, (t0 + row < ctx) ? B.v[pg][i] : uint4{0, 0, 0, 0});
+        const uint4 vv = (t0 + row < ctx) ? B.v[pg][i] : uint4{0, 0, 0, 0};
+        if constexpr (KV8) {
+          uint4 lo, hi;
+          e4m3x16_to_bf16(B.k[pg][i], lo, hi);
+          st16(kstage + row * C::KPITCH + col * 2, lo);
+          st16(kstage + row * C::KPITCH + col * 2 + 16, hi);
+          e4m3x16_to_bf16(vv, lo, hi);
+          st16(vstage + row * C::VPITCH + col * 2, lo);
+          st16(vstage + row * C::VPITCH + col * 2 + 16, hi);
+        } else {
+          st16(kstage + row * C::KPITCH + col * 2, B.k[pg][i]);
+          st16(vstage + row * C::VPITCH + col * 2, vv);
+        }
       }
     // The staged rows are read back by this wave only; keep the compiler from moving reads up.
     __asm__ volatile("" ::: "memory");
@@ -292,7 +310,7 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
     __asm__ volatile("" ::: "memory");
   };
 
-  DecBuf<HD> A;
+  DecBuf<HD, E> A;
   for (int u = wave; u < units; u += kDecWaves) {
     load(u, A);
     compute(u, A);
@@ -314,7 +332,7 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   }
   __syncthreads();
   merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, A_.max_splits, num_q_heads, A_.ws_o, A_.ws_ml, A_.out,
-                  A_.out_bf16);
+                  A_.out_bf16, A_.v_scale);
 }
 
 // Work plan of the persistent decode.  A piece is one (sequence, split) pair; its length in
@@ -386,7 +404,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 // holds only items with i % 8 == q % 8, so with Hkv = 8 each KV head stays on one XCD and blocks
 // shared between sequences stay in that XCD's L2.  The item after next is fetched while the
 // current item runs; the next item's block ids and query are loaded then too.
-template <int HD, bool CHECK, bool NARROW>
+template <int HD, bool CHECK, bool NARROW, bool KV8>
 __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, const int2* __restrict__ pieces,
                                                                   int32_t* __restrict__ plan, int queues) {
   __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
@@ -422,7 +440,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, con
       for (int i = tid; i < a.group * HD; i += kDecThreads)
         store_out(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + cur.g * a.group) * HD + i, 0.f, a.out_bf16);
     } else {
-      decode_bf16_item<HD, CHECK, NARROW>(a, cur, smem);
+      decode_bf16_item<HD, CHECK, NARROW, KV8>(a, cur, smem);
     }
     if (tid == 0) fetched[p] = after;
     __syncthreads();  // the next item reuses the staging and merge areas; fetched[p] is published
@@ -556,7 +574,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_f32_kernel(
     }
   }
   __syncthreads();
-  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16);
+  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16,
+                  1.f);
 }
 
 // Log-sum-exp merge of split partials: grid (num_kv_heads, num_seqs); the 256 threads cover the
@@ -700,20 +719,26 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
   return ws_layout(num_seqs, num_q_heads, head_dim, max_splits).total;
 }
 
-extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
-                                            const void* value_pool, const int32_t* block_tables,
-                                            int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                            int32_t head_dim, int32_t num_blocks, float scale, pkv_dtype dtype,
-                                            int32_t split_tokens, void* workspace, size_t workspace_bytes,
-                                            int32_t* err_flag, void* stream) {
+namespace {
+
+// Shared body of the bf16 / fp32 and FP8 decode calls.  dtype is the pool dtype (FP8_E4M3 pools take
+// bf16 queries and the two scales).
+pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                       const void* value_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t num_blocks, float scale, pkv_dtype dtype, float k_scale,
+                       float v_scale, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                       int32_t* err_flag, void* stream) {
+  const bool kv8 = dtype == PKV_DTYPE_FP8_E4M3;
+  if (kv8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f)))
+    return PKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0)
     return PKV_ERR_INVALID_ARG;
   if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 2048) return PKV_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return PKV_ERR_UNSUPPORTED;
-  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16 && !kv8) return PKV_ERR_UNSUPPORTED;
   if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid y/z limits
@@ -734,7 +759,7 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
   float* ws_o = max_splits > 1 ? reinterpret_cast<float*>(ws + lay.o) : nullptr;
   float* ws_ml = max_splits > 1 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
   const int group = num_q_heads / num_kv_heads;
-  const float scale_log2 = scale * kLog2e;
+  const float scale_log2 = kv8 ? scale * kLog2e * k_scale : scale * kLog2e;
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   dim3 grid(max_splits, num_kv_heads, num_seqs);
@@ -750,17 +775,18 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
     case 128: PKV_DEC(KERNEL, T, 128, CHECK); break; \
     default: PKV_DEC(KERNEL, T, 256, CHECK); break;  \
   }
-  if (dtype == PKV_DTYPE_BF16) {
-    DecArgs a{static_cast<const uint16_t*>(query), static_cast<const uint16_t*>(key_pool),
-              static_cast<const uint16_t*>(value_pool), block_tables, context_lens, ws_o, ws_ml, out, err_flag,
-              max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, max_splits, ob, scale_log2};
+  if (dtype == PKV_DTYPE_BF16 || kv8) {
+    DecArgs a{static_cast<const uint16_t*>(query), key_pool, value_pool, block_tables, context_lens, ws_o, ws_ml, out,
+              err_flag, max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, max_splits, ob,
+              scale_log2, kv8 ? v_scale : 1.f};
     // Two resident workgroups per CU at head_dim <= 128 (register bound), one at 256; never more
     // workgroups than the largest possible number of items.
     const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * max_splits;
     const int64_t resident = static_cast<int64_t>(pkv_host::cu_count()) * (head_dim <= 128 ? 2 : 1);
     const unsigned nwg = static_cast<unsigned>(max_items < resident ? max_items : resident);
     const int queues = nwg % kMaxQueues == 0 ? kMaxQueues : (nwg % 8 == 0 ? 8 : 1);
-    const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
+    const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) <
+                            (1ull << 32) &&
                         num_blocks < (1 << 24);
     if (err_flag)
       hipLaunchKernelGGL((decode_plan_kernel<true>), dim3(1), dim3(kPlanThreads), 0, st, context_lens, num_seqs,
@@ -769,11 +795,13 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
       hipLaunchKernelGGL((decode_plan_kernel<false>), dim3(1), dim3(kPlanThreads), 0, st, context_lens, num_seqs,
                          max_blocks_per_seq, S, pieces, plan, static_cast<int>(nwg), queues, err_flag);
     if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
-#define PKV_DEC_BF16(HD, CHECK, NARROW)                                                                    \
-  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW>), dim3(nwg), dim3(kDecThreads), 0, st, a, pieces, \
+#define PKV_DEC_BF16(HD, CHECK, NARROW, KV8)                                                                    \
+  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW, KV8>), dim3(nwg), dim3(kDecThreads), 0, st, a, pieces, \
                      plan, queues)
+#define PKV_DEC_BF16_K(HD, CHECK, NARROW) \
+  if (kv8) PKV_DEC_BF16(HD, CHECK, NARROW, true); else PKV_DEC_BF16(HD, CHECK, NARROW, false);
 #define PKV_DEC_BF16_N(HD, CHECK) \
-  if (narrow) PKV_DEC_BF16(HD, CHECK, true); else PKV_DEC_BF16(HD, CHECK, false);
+  if (narrow) { PKV_DEC_BF16_K(HD, CHECK, true) } else { PKV_DEC_BF16_K(HD, CHECK, false) }
 #define PKV_DEC_BF16_C(HD) \
   if (err_flag) { PKV_DEC_BF16_N(HD, true) } else { PKV_DEC_BF16_N(HD, false) }
     switch (head_dim) {
@@ -783,6 +811,7 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
     }
 #undef PKV_DEC_BF16_C
 #undef PKV_DEC_BF16_N
+#undef PKV_DEC_BF16_K
 #undef PKV_DEC_BF16
   } else {
     if (err_flag) { PKV_DEC_HD(decode_f32_kernel, float, true) } else { PKV_DEC_HD(decode_f32_kernel, float, false) }
@@ -796,4 +825,32 @@ extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, cons
     return pkv_host::launch_status();
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                            const void* value_pool, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t num_blocks, float scale, pkv_dtype dtype,
+                                            int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                            int32_t* err_flag, void* stream) {
+  if (dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // FP8 pools need their scales
+  return decode_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale, dtype, 1.f, 1.f, split_tokens,
+                     workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_fp8(void* out, pkv_dtype out_dtype, const void* query,
+                                                const void* key_pool, const void* value_pool,
+                                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                                float scale, float k_scale, float v_scale, int32_t split_tokens,
+                                                void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                                void* stream) {
+  return decode_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale, PKV_DTYPE_FP8_E4M3, k_scale,
+                     v_scale, split_tokens, workspace, workspace_bytes, err_flag, stream);
 }

@@ -39,7 +39,8 @@ constexpr int kPreTile = 4 * kPreRows;          // query rows per workgroup
 constexpr float kMaxWeight = 1048576.f;         // 2^20: largest softmax weight before the reference max moves
 constexpr int kIdWindow = 2048;                 // block ids held in LDS (32,768 positions)
 
-template <int HD>
+// E: bytes per pool element (2 for bf16, 1 for E4M3 codes); LDS tiles are bf16 either way.
+template <int HD, int E = 2>
 struct PreCfg {
   static constexpr int KT = HD == 256 ? 32 : 64;  // key positions per LDS tile
   static constexpr int MS = KT / 32;              // 32-key row tiles of S^T
@@ -48,7 +49,8 @@ struct PreCfg {
   static constexpr int MD = HD / 32;              // 32-row tiles of O^T
   static constexpr int KPITCH = HD * 2 + 16;      // LDS bytes per K row (conflict-free 16-byte reads)
   static constexpr int VPITCH = HD * 2 + 64;      // LDS bytes per V row (transposed reads without bank conflicts)
-  static constexpr int CPR = HD / 8;              // 16-byte chunks per row
+  static constexpr int EPC = 16 / E;              // pool elements per 16-byte chunk
+  static constexpr int CPR = HD / EPC;            // 16-byte chunks per row
   static constexpr int TILE = KT * (KPITCH + VPITCH);
   static constexpr int LOADS = 2 * KT * CPR / kPreThreads;  // chunks per thread per tensor per tile pair
   static constexpr int LDS = 4 * TILE;                       // two buffers of a tile pair
@@ -57,14 +59,17 @@ struct PreCfg {
   static_assert(LOADS * kPreThreads == 2 * KT * CPR, "pair loads must divide evenly");
 };
 
-template <int HD, bool CHECK, bool NARROW>
+// KV8: the pools hold E4M3 codes, converted exactly to bf16 on their way into LDS; scale_log2 then
+// includes the K scale and v_scale multiplies the output (1 for bf16 pools).
+template <int HD, bool CHECK, bool NARROW, bool KV8>
 __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
     const uint16_t* __restrict__ query, const int32_t* __restrict__ cu_q_lens,
-    const int32_t* __restrict__ chunk_offsets, const uint16_t* __restrict__ key_pool,
-    const uint16_t* __restrict__ value_pool, const int32_t* __restrict__ block_tables, int max_blocks, int q_tiles,
-    int num_q_heads, int num_kv_heads, int group, int num_blocks, int causal, float scale_log2,
+    const int32_t* __restrict__ chunk_offsets, const void* __restrict__ key_pool,
+    const void* __restrict__ value_pool, const int32_t* __restrict__ block_tables, int max_blocks, int q_tiles,
+    int num_q_heads, int num_kv_heads, int group, int num_blocks, int causal, float scale_log2, float v_scale,
     void* __restrict__ out, int out_bf16, int32_t* err_flag) {
-  using C = PreCfg<HD>;
+  constexpr int E = KV8 ? 1 : 2;
+  using C = PreCfg<HD, E>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __shared__ int ids[kIdWindow];  // block ids of logical blocks [win0, win0 + kIdWindow)
 
@@ -129,8 +134,8 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
   // every i and only the block id changes.
   constexpr int RPI = kPreThreads / C::CPR;  // pair rows per load round
   const int t_row = threadIdx.x / C::CPR;
-  const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * 2);
-  const uint32_t c0 = static_cast<uint32_t>(((t_row % kBlockSize) * num_kv_heads + g) * HD * 2 + (threadIdx.x % C::CPR) * 16);
+  const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * E);
+  const uint32_t c0 = static_cast<uint32_t>(((t_row % kBlockSize) * num_kv_heads + g) * HD * E + (threadIdx.x % C::CPR) * 16);
   uint4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_pair = [&](int p) {
     const int key0p = 2 * p * C::KT + t_row;
@@ -163,10 +168,20 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
       const int f = threadIdx.x + kPreThreads * i;
       const int tt = f / (C::KT * C::CPR);
       const int rem = f - tt * (C::KT * C::CPR);
-      const int row = rem / C::CPR, col = (rem % C::CPR) * 8;
+      const int row = rem / C::CPR, col = (rem % C::CPR) * C::EPC;
       char* base = smem + (2 * buf + tt) * C::TILE;
-      st16(base + row * C::KPITCH + col * 2, kreg[i]);
-      st16(base + C::KT * C::KPITCH + row * C::VPITCH + col * 2, vreg[i]);
+      if constexpr (KV8) {
+        uint4 lo, hi;
+        e4m3x16_to_bf16(kreg[i], lo, hi);
+        st16(base + row * C::KPITCH + col * 2, lo);
+        st16(base + row * C::KPITCH + col * 2 + 16, hi);
+        e4m3x16_to_bf16(vreg[i], lo, hi);
+        st16(base + C::KT * C::KPITCH + row * C::VPITCH + col * 2, lo);
+        st16(base + C::KT * C::KPITCH + row * C::VPITCH + col * 2 + 16, hi);
+      } else {
+        st16(base + row * C::KPITCH + col * 2, kreg[i]);
+        st16(base + C::KT * C::KPITCH + row * C::VPITCH + col * 2, vreg[i]);
+      }
     }
   };
 
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
   const float fa = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - M);
   const float fb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - M);
   const float Ls = fa * l_run + fb * lb;
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  const float inv = Ls > 0.f ? v_scale / Ls : 0.f;
   const float ia = fa * inv, ib = fb * inv;
   const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
 #pragma unroll
@@ -357,19 +372,23 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(
 
 using namespace pkv;
 
-extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* query,
-                                                   const int32_t* cu_q_lens, const int32_t* chunk_offsets,
-                                                   const void* key_pool, const void* value_pool,
-                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                                   int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
-                                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-                                                   int32_t causal, float scale, pkv_dtype dtype, int32_t* err_flag,
-                                                   void* stream) {
+namespace {
+
+// Shared body of the bf16 and FP8 prefill calls (dtype = pool dtype; queries are bf16).
+pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const int32_t* cu_q_lens,
+                        const int32_t* chunk_offsets, const void* key_pool, const void* value_pool,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_q_len,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                        int32_t causal, float scale, pkv_dtype dtype, float k_scale, float v_scale,
+                        int32_t* err_flag, void* stream) {
+  const bool kv8 = dtype == PKV_DTYPE_FP8_E4M3;
+  if (kv8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f)))
+    return PKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || max_q_len < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0 || !std::isfinite(scale) || !(scale > 0.f))
     return PKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
-  if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (dtype != PKV_DTYPE_BF16 && !kv8) return PKV_ERR_UNSUPPORTED;
   if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
@@ -382,19 +401,22 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
   const int64_t items = static_cast<int64_t>(num_seqs) * num_q_heads * q_tiles;
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
-  const float scale_log2 = scale * kLog2e;
+  const float scale_log2 = kv8 ? scale * kLog2e * k_scale : scale * kLog2e;
+  const float vs = kv8 ? v_scale : 1.f;
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
+  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) <
+                          (1ull << 32) &&
                       num_blocks < (1 << 24);
-#define PKV_PRE(HD, CHECK, NARROW)                                                                                \
-  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK, NARROW>), dim3(static_cast<unsigned>(items)),               \
+#define PKV_PRE(HD, CHECK, NARROW, KV8)                                                                           \
+  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK, NARROW, KV8>), dim3(static_cast<unsigned>(items)),          \
                      dim3(kPreThreads), 0, st, static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets,    \
-                     static_cast<const uint16_t*>(key_pool), static_cast<const uint16_t*>(value_pool),           \
-                     block_tables, max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks,    \
-                     causal != 0, scale_log2, out, ob, err_flag)
+                     key_pool, value_pool, block_tables, max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, \
+                     group, num_blocks, causal != 0, scale_log2, vs, out, ob, err_flag)
+#define PKV_PRE_K(HD, CHECK, NARROW) \
+  if (kv8) PKV_PRE(HD, CHECK, NARROW, true); else PKV_PRE(HD, CHECK, NARROW, false);
 #define PKV_PRE_N(HD, CHECK) \
-  if (narrow) PKV_PRE(HD, CHECK, true); else PKV_PRE(HD, CHECK, false);
+  if (narrow) { PKV_PRE_K(HD, CHECK, true) } else { PKV_PRE_K(HD, CHECK, false) }
 #define PKV_PRE_HD(CHECK)                         \
   switch (head_dim) {                             \
     case 64: PKV_PRE_N(64, CHECK) break;          \
@@ -404,6 +426,36 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
   if (err_flag) { PKV_PRE_HD(true) } else { PKV_PRE_HD(false) }
 #undef PKV_PRE_HD
 #undef PKV_PRE_N
+#undef PKV_PRE_K
 #undef PKV_PRE
   return pkv_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* query,
+                                                   const int32_t* cu_q_lens, const int32_t* chunk_offsets,
+                                                   const void* key_pool, const void* value_pool,
+                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                   int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                                   int32_t causal, float scale, pkv_dtype dtype, int32_t* err_flag,
+                                                   void* stream) {
+  if (dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // FP8 pools need their scales
+  return prefill_impl(out, out_dtype, query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
+                      max_blocks_per_seq, num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, causal,
+                      scale, dtype, 1.f, 1.f, err_flag, stream);
+}
+
+extern "C" pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_dtype, const void* query,
+                                                       const int32_t* cu_q_lens, const int32_t* chunk_offsets,
+                                                       const void* key_pool, const void* value_pool,
+                                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                       int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                                       int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                                       int32_t causal, float scale, float k_scale, float v_scale,
+                                                       int32_t* err_flag, void* stream) {
+  return prefill_impl(out, out_dtype, query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
+                      max_blocks_per_seq, num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, causal,
+                      scale, PKV_DTYPE_FP8_E4M3, k_scale, v_scale, err_flag, stream);
 }

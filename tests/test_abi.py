@@ -89,6 +89,26 @@ def test_host_validation_rejects_bad_arguments():
     assert cw(null, null, 100, 512, null, null, null, 4, 10, 8, 64, 16, 1, null, null) == 1
     assert cw(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 1, null, null) == 1
     assert cw(null, null, 512, 512, null, null, null, 0, 10, 8, 64, 16, 1, null, null) == 0
+    # FP8 pools: the generic calls refuse them (they need scales); the *_fp8 calls check scales,
+    # input dtype and pointers before any device work.
+    assert dec(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 2, 0, null, 0, null, null) == 2
+    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 2, null, null) == 2
+    assert cw(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 2, null, null) == 2
+    d8 = lib.pkv_paged_attn_decode_fp8
+    assert d8(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 0.0, 1.0, 0, null, 0, null, null) == 1
+    assert d8(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 1.0, float("inf"), 0, null, 0, null,
+              null) == 1
+    assert d8(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 1.0, 1.0, 0, null, 0, null, null) == 1
+    assert d8(null, 0, null, null, null, null, 8, null, 0, 8, 8, 64, 10, 0.1, 1.0, 1.0, 0, null, 0, null, null) == 0
+    p8 = lib.pkv_paged_attn_prefill_chunk_fp8
+    assert p8(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, -1.0, 1.0, null, null) == 1
+    assert p8(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 1.0, 1.0, null, null) == 1
+    assert p8(null, 0, null, null, null, null, null, null, 8, 0, 10, 8, 8, 64, 10, 1, 0.1, 1.0, 1.0, null, null) == 0
+    w8 = lib.pkv_cache_write_fp8
+    assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 2, 1.0, 1.0, null, null) == 2  # fp8 input
+    assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 1, float("nan"), 1.0, null, null) == 1
+    assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 1, 1.0, 1.0, null, null) == 1
+    assert w8(null, null, 512, 512, null, null, null, 0, 10, 8, 64, 16, 0, 1.0, 1.0, null, null) == 0
     # Slot mapping.
     sm = lib.pkv_slot_mapping
     assert sm(null, null, 4, null, null, 2, 5, 10, 8, null, null) == 2
@@ -96,9 +116,12 @@ def test_host_validation_rejects_bad_arguments():
     assert sm(null, null, 4, null, null, 0, 5, 10, 16, null, null) == 0
 
 
-@pytest.mark.parametrize("name", ["pkv_cache_write", "pkv_paged_attn_decode", "pkv_paged_attn_prefill_chunk"])
+@pytest.mark.parametrize("name", ["pkv_cache_write", "pkv_paged_attn_decode", "pkv_paged_attn_prefill_chunk",
+                                  "pkv_cache_write_fp8", "pkv_paged_attn_decode_fp8",
+                                  "pkv_paged_attn_prefill_chunk_fp8"])
 def test_header_documents_each_call(name):
     text = open(HEADER).read()
     i = text.index(name + "(")
     block = text[max(0, i - 2500):i]
-    assert "/*" in block and ("Chunked Prefill" in block or "Chunked-Prefill" in block or "C13" in block)
+    assert "/*" in block and any(tag in block for tag in ("Chunked Prefill", "Chunked-Prefill", "C13",
+                                                          "vLLM-internals", "Engine-core"))

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.fp8 import E4M3_MAX, NAN_CODE, dequantize, e4m3_decode, e4m3_encode, e4m3_value, quantize
+from oracle.fp8 import (E4M3_MAX, NAN_CODE, dequantize, e4m3_decode, e4m3_encode, e4m3_value, quantize,
+                        quantize_bf16_bits)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -85,3 +86,11 @@ def test_quantisation_error_bound_and_monotonicity():
     order = np.argsort(xs)
     vals = e4m3_decode(quantize(xs[order].astype(np.float32), scale))
     assert np.all(np.diff(vals) >= 0)
+
+
+def test_bf16_table_form_equals_direct_form():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 65536, 50000, dtype=np.uint32).astype(np.uint16)
+    f = (bits.astype(np.uint32) << 16).view(np.float32)
+    for scale in (0.0123, 1.0, 3.5):
+        assert np.array_equal(quantize_bf16_bits(bits, scale), quantize(f, scale))
