@@ -277,6 +277,41 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = 5 * kp.numel() * kp.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
+    # Fused mixed-batch launch against the two separate attention calls (same inputs, same pools).
+    fused_info = None
+    if pre is not None:
+        fkp, fvp = (kp8, vp8) if fp8 else (kp, vp)
+        sc = (k_scale, v_scale) if fp8 else (1.0, 1.0)
+
+        def fused():
+            pkv.paged_attn_mixed(fkp, fvp, dec.scale, dec_query=d_q, dec_block_tables=d_bt, context_lens=d_ctx,
+                                 pre_query=p_q, cu_q_lens=p_cu, chunk_offsets=p_off, pre_block_tables=p_bt,
+                                 max_q_len=p_maxl, causal=True, k_scale=sc[0], v_scale=sc[1], dec_out=d_out,
+                                 pre_out=p_out, workspace=ws)
+
+        def separate():
+            if fp8:
+                pkv.paged_attn_decode_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, out=d_out,
+                                          workspace=ws)
+                pkv.paged_attn_prefill_chunk_fp8(p_q, p_cu, p_off, kp8, vp8, p_bt, p_maxl, pre.scale, k_scale,
+                                                 v_scale, causal=True, out=p_out)
+            else:
+                pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=d_out, workspace=ws)
+                pkv.paged_attn_prefill_chunk(p_q, p_cu, p_off, kp, vp, p_bt, p_maxl, pre.scale, causal=True,
+                                             out=p_out)
+
+        times = {}
+        for name, fn in (("separate", separate), ("fused", fused), ("separate", separate), ("fused", fused)):
+            fn()
+            e0.record(stream)
+            for _ in range(10):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[name] = min(times.get(name, 1e9), e0.elapsed_time(e1) / 10)
+        fused_info = {"fused_ms": times["fused"], "separate_ms": times["separate"],
+                      "speedup": times["separate"] / times["fused"]}
+
     # Copy-on-write block copies on this pool: 512 disjoint pairs (K and V, read + written).
     nblk = dec.num_blocks
     cp = torch.randperm(nblk, device="cpu")[:1024].to(torch.int32)
@@ -322,6 +357,7 @@ def main():
         "decode_kv_bytes_logical": dec_kv_logical,
         "stream_read_gbs": stream_gbs,
         "decode_frac_of_stream_read": dec_gbs / stream_gbs,
+        "fused_mixed_step": fused_info,
         "copy_blocks": copy_info,
         "block_manager_host": bm_info,
     }

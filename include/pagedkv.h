@@ -248,6 +248,53 @@ pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_dtype, cons
                                             int32_t* err_flag, void* stream);
 
 /*
+ * Token-budget step composer (host code; [Chunked-Prefill], token-budget section: each step adds one
+ * token per running decode first, then fills the rest of the budget with chunks of waiting prompts,
+ * and a prompt that does not fit goes on in the next step; [vLLM-internals], scheduler loop).
+ *   num_decode            running sequences that each want one decode token, in priority order; if
+ *                         they exceed the budget only the first token_budget are scheduled (a reading:
+ *                         the pages do not say)
+ *   prefill_remaining     int32 [num_prefill], prompt tokens not yet prefilled, queue order, each > 0
+ *   token_budget          tokens per step (> 0)
+ *   max_chunk             cap on one prompt's chunk (<= 0: none); budget a capped prompt leaves goes on
+ *                         to the next prompt
+ *   chunk_len             out int32 [num_prefill]: tokens of each prompt scheduled this step (0 = none)
+ *   num_decode_scheduled  out: decode tokens scheduled
+ * Returns PKV_ERR_INVALID_ARG (writing nothing) on a bad argument.  Pointers are host memory.
+ */
+pkv_status pkv_compose_step(int32_t num_decode, const int32_t* prefill_remaining, int32_t num_prefill,
+                            int32_t token_budget, int32_t max_chunk, int32_t* chunk_len,
+                            int32_t* num_decode_scheduled);
+
+/*
+ * Fused mixed-batch step ([vLLM-internals], scheduler-loop section: one step carries the decode
+ * tokens and the prefill chunks through one forward call; [Chunked-Prefill], token-budget section).
+ * One attention launch (plus the decode's plan pass and, for long contexts, its split reduce) that
+ * computes exactly what pkv_paged_attn_decode computes for the decode arguments and what
+ * pkv_paged_attn_prefill_chunk computes for the prefill arguments, over the same pools; outputs are
+ * bit-identical to those two calls.  Either part may be empty (num_dec_seqs == 0, or
+ * num_pre_seqs == 0 / max_q_len == 0).
+ *   decode part   dec_out / dec_query [num_dec_seqs, num_q_heads, head_dim], dec_block_tables
+ *                 [num_dec_seqs, dec_max_blocks], context_lens [num_dec_seqs]
+ *   prefill part  pre_out / pre_query [cu_q_lens[num_pre_seqs], num_q_heads, head_dim], cu_q_lens,
+ *                 chunk_offsets, pre_block_tables [num_pre_seqs, pre_max_blocks], max_q_len, causal
+ *   dtype         BF16 pools, or FP8_E4M3 pools with k_scale / v_scale (ignored for BF16); queries bf16
+ *   split_tokens, workspace  as for pkv_paged_attn_decode with the decode part's shapes
+ * head_dim 64 or 128 (a decode workgroup runs two decode workers side by side); 256 is
+ * PKV_ERR_UNSUPPORTED.
+ */
+pkv_status pkv_paged_attn_mixed(void* dec_out, const void* dec_query, const int32_t* dec_block_tables,
+                                int32_t dec_max_blocks, const int32_t* context_lens, int32_t num_dec_seqs,
+                                void* pre_out, const void* pre_query, const int32_t* cu_q_lens,
+                                const int32_t* chunk_offsets, const int32_t* pre_block_tables,
+                                int32_t pre_max_blocks, int32_t num_pre_seqs, int32_t max_q_len, int32_t causal,
+                                const void* key_pool, const void* value_pool, int32_t num_blocks,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+                                pkv_dtype dtype, float k_scale, float v_scale, pkv_dtype out_dtype,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                void* stream);
+
+/*
  * Block copy for copy-on-write ([Engine-core] §1.5; [C13-L2] 改进二, sharing paragraph): for each
  * pair i, the whole block src[i] (16 rows x num_kv_heads x head_dim, K and V) is copied bit for bit
  * to block dst[i].  src / dst: int32 [num_pairs] device arrays; src[i] == dst[i] is a no-op; a

@@ -52,6 +52,10 @@ _SIGS = {
                                          _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk_fp8": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                                 _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _vp]),
+    "pkv_paged_attn_mixed": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _f32, _f32, _i32, _i32, _vp, _sz,
+                                    _vp, _vp]),
+    "pkv_compose_step": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp]),
     "pkv_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_bm_state_bytes": (_sz, [_i32]),
@@ -203,6 +207,20 @@ def copy_blocks(key_pool: torch.Tensor, value_pool: torch.Tensor, src: torch.Ten
     _check(_lib.pkv_copy_blocks(_ptr(key_pool), _ptr(value_pool), _ptr(src), _ptr(dst), src.shape[0], nblk, hkv, hd,
                                 bs, _dtype_code(key_pool), _ptr(err_flag), _stream(key_pool.device)),
            "pkv_copy_blocks")
+
+
+def compose_step(num_decode: int, prefill_remaining, token_budget: int, max_chunk: int = 0):
+    """Token-budget composition of one step (decode tokens first, then prompt chunks in queue
+    order); returns (decode tokens scheduled, chunk length per waiting prompt).  Host code."""
+    import numpy as np
+    rem = np.ascontiguousarray(prefill_remaining, dtype=np.int32)
+    chunks = np.zeros(rem.shape[0], dtype=np.int32)
+    nd = ctypes.c_int32(0)
+    _check(_lib.pkv_compose_step(int(num_decode), ctypes.c_void_p(rem.ctypes.data) if rem.size else None,
+                                 rem.shape[0], int(token_budget), int(max_chunk),
+                                 ctypes.c_void_p(chunks.ctypes.data) if rem.size else None, ctypes.byref(nd)),
+           "pkv_compose_step")
+    return nd.value, chunks
 
 
 class BlockManager:
@@ -420,6 +438,65 @@ def paged_attn_prefill_chunk_fp8(query: torch.Tensor, cu_q_lens: torch.Tensor, c
                                                  float(k_scale), float(v_scale), _ptr(err_flag),
                                                  _stream(query.device)), "pkv_paged_attn_prefill_chunk_fp8")
     return out
+
+
+def paged_attn_mixed(key_pool: torch.Tensor, value_pool: torch.Tensor, scale: float,
+                     dec_query: torch.Tensor | None = None, dec_block_tables: torch.Tensor | None = None,
+                     context_lens: torch.Tensor | None = None, pre_query: torch.Tensor | None = None,
+                     cu_q_lens: torch.Tensor | None = None, chunk_offsets: torch.Tensor | None = None,
+                     pre_block_tables: torch.Tensor | None = None, max_q_len: int = 0, causal: bool = True,
+                     k_scale: float = 1.0, v_scale: float = 1.0, dec_out: torch.Tensor | None = None,
+                     pre_out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                     workspace: torch.Tensor | None = None, split_tokens: int = 0,
+                     err_flag: torch.Tensor | None = None):
+    """Decode tokens and prefill chunks of one step in one fused launch; see pkv_paged_attn_mixed.
+    Returns (decode output or None, prefill output or None).  bf16 or E4M3 pools (with scales)."""
+    _need_gpu(key_pool, value_pool, dec_query, dec_block_tables, context_lens, pre_query, cu_q_lens, chunk_offsets,
+              pre_block_tables, dec_out, pre_out, workspace, err_flag)
+    _need_i32(dec_block_tables, context_lens, cu_q_lens, chunk_offsets, pre_block_tables, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    code = _dtype_code(key_pool)
+    if code not in (DTYPE_BF16, DTYPE_FP8_E4M3):
+        raise ValueError("pools must be bf16 or FP8 E4M3")
+    hq = None
+    nd = 0
+    if dec_query is not None:
+        if dec_query.dim() != 3 or dec_query.shape[2] != hd or dec_query.dtype != torch.bfloat16 \
+                or not dec_query.is_contiguous():
+            raise ValueError("dec_query must be contiguous bf16 [num_seqs, num_q_heads, head_dim]")
+        nd, hq = dec_query.shape[0], dec_query.shape[1]
+        if context_lens.shape[0] != nd or dec_block_tables.shape[0] != nd:
+            raise ValueError("decode batch sizes differ")
+        if dec_out is None:
+            dec_out = torch.empty((nd, hq, hd), dtype=out_dtype, device=dec_query.device)
+        if workspace is None:
+            workspace = decode_workspace(dec_query, hkv, dec_block_tables.shape[1], split_tokens)
+    npre = 0
+    if pre_query is not None:
+        if pre_query.dim() != 3 or pre_query.shape[2] != hd or pre_query.dtype != torch.bfloat16 \
+                or not pre_query.is_contiguous():
+            raise ValueError("pre_query must be contiguous bf16 [rows, num_q_heads, head_dim]")
+        if hq is not None and pre_query.shape[1] != hq:
+            raise ValueError("decode and prefill queries must have the same head count")
+        hq = pre_query.shape[1]
+        npre = chunk_offsets.shape[0]
+        if cu_q_lens.shape[0] != npre + 1 or pre_block_tables.shape[0] != npre:
+            raise ValueError("prefill batch sizes differ")
+        if pre_out is None:
+            pre_out = torch.empty((pre_query.shape[0], hq, hd), dtype=out_dtype, device=pre_query.device)
+    if hq is None:
+        return None, None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    out_code = _dtype_code(dec_out if dec_out is not None else pre_out)
+    _check(_lib.pkv_paged_attn_mixed(_ptr(dec_out), _ptr(dec_query), _ptr(dec_block_tables),
+                                     0 if dec_block_tables is None else dec_block_tables.shape[1], _ptr(context_lens),
+                                     nd, _ptr(pre_out), _ptr(pre_query), _ptr(cu_q_lens), _ptr(chunk_offsets),
+                                     _ptr(pre_block_tables), 0 if pre_block_tables is None else pre_block_tables.shape[1],
+                                     npre, int(max_q_len), int(bool(causal)), _ptr(key_pool), _ptr(value_pool), nblk, hq,
+                                     hkv, hd, float(scale), code, float(k_scale), float(v_scale), out_code,
+                                     int(split_tokens), _ptr(workspace), ws_bytes, _ptr(err_flag),
+                                     _stream(key_pool.device)), "pkv_paged_attn_mixed")
+    return dec_out, pre_out
 
 
 def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:

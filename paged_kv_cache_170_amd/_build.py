@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["status.hip", "cache.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
+SOURCES = ["status.hip", "cache.hip", "decode.hip", "prefill.hip", "mixed.hip", "block_manager.cpp", "scheduler.cpp"]
 LIB_NAME = "libpagedkv.so"
 ARCH = "gfx950"
 

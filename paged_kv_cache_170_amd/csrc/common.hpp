@@ -77,6 +77,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Largest softmax weight (2^20) before the attention kernels raise their reference max.
+constexpr float kMaxWeight = 1048576.f;
+
+// Barrier of the whole workgroup.
+struct WgSync {
+  __device__ void operator()() const { __syncthreads(); }
+};
+
+// Barrier of one 256-thread half (waves 4h .. 4h + 3) of a 512-thread workgroup, so that the two
+// halves can run separate programs: each wave adds one arrival to the half's LDS counter (zero at
+// start) and waits until all four waves of the current round have arrived.  The wait is bounded
+// (about 2^22 polls of 64 cycles) so that a wave can never spin forever.
+struct HalfSync {
+  int* cnt;
+  int target;
+  __device__ void operator()() {
+    target += 4;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spins = 0; spins < (1 << 22); ++spins) {
+      if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= target)
+        break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+};
+
 // Sixteen E4M3 codes (one 16-byte load, element i in byte i) to sixteen bf16 values in the same
 // order.  Exact: every E4M3 value is a bf16 value (the conversion's scale operand is 1).
 __device__ __forceinline__ void e4m3x16_to_bf16(uint4 c, uint4& lo, uint4& hi) {
