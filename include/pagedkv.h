@@ -267,6 +267,51 @@ pkv_status pkv_compose_step(int32_t num_decode, const int32_t* prefill_remaining
                             int32_t* num_decode_scheduled);
 
 /*
+ * Iteration-level scheduler over synthetic requests (host code; [vLLM-internals], scheduler-loop
+ * section and its four modes; [Engine-core] §2.3).  Each step it releases finished requests and
+ * their blocks, admits waiting requests in queue order (only arrived ones, while a running slot is
+ * free and the block manager can hold the request's whole final length), then assigns every running
+ * request its work: a prompt (whole, or a chunk) or one decode token.  Modes:
+ *   PKV_SCHED_NAIVE       one request at a time
+ *   PKV_SCHED_STATIC      a batch is admitted only when the previous one has fully finished; a
+ *                         finished request keeps its slot until its whole batch is done
+ *   PKV_SCHED_CONTINUOUS  admission and release every step; a newly admitted prompt is prefilled
+ *                         whole in its first step
+ *   PKV_SCHED_CHUNKED     as CONTINUOUS, with the step composed under token_budget by the rule of
+ *                         pkv_compose_step (decode tokens first, then prompt chunks, max_chunk cap)
+ * The first output token of a request is produced by the step that finishes its prompt; each
+ * later step gives one more token; a request is done after output_len tokens.  Block-table rows
+ * live in the scheduler (pkv_sched_table, [max_running][max_blocks]); rows are filled through the
+ * block manager whose state the caller passes (not shared with other users while in use).  All
+ * pointers are host memory; the state is one caller-owned, 8-byte aligned buffer.
+ */
+typedef enum { PKV_SCHED_NAIVE = 0, PKV_SCHED_STATIC = 1, PKV_SCHED_CONTINUOUS = 2, PKV_SCHED_CHUNKED = 3 } pkv_sched_mode;
+
+size_t pkv_sched_state_bytes(int32_t max_requests, int32_t max_running, int32_t max_blocks, int64_t max_itl_samples);
+pkv_status pkv_sched_init(void* state, size_t state_bytes, int32_t mode, int32_t max_requests, int32_t max_running,
+                          int32_t max_blocks, int64_t max_itl_samples, int32_t token_budget, int32_t max_chunk,
+                          void* bm_state);
+/* Requests arrive in id order (arrival times non-decreasing, any time unit); prompt_len, output_len > 0. */
+pkv_status pkv_sched_add_request(void* state, int32_t prompt_len, int32_t output_len, double arrival, int32_t* id);
+/* Plan the step starting at `now`.  Outputs (arrays of max_running entries): decode entries (table row,
+ * context length counting the new token, whose K/V the step writes at position ctx - 1) and prompt
+ * chunks (table row, first position, length; the step writes positions [offset, offset + len) and the
+ * chunk attends causally to [0, offset + len)).  next_arrival: arrival of the next waiting request,
+ * -1 if none (when nothing is planned the caller advances its clock to it). */
+pkv_status pkv_sched_plan(void* state, double now, int32_t* num_decode, int32_t* dec_row, int32_t* dec_ctx,
+                          int32_t* num_chunks, int32_t* chunk_row, int32_t* chunk_offset, int32_t* chunk_len,
+                          double* next_arrival);
+/* The planned step ended at `now`: record its tokens and release finished requests. */
+pkv_status pkv_sched_complete(void* state, double now);
+const int32_t* pkv_sched_table(const void* state);
+int32_t pkv_sched_num_done(const void* state);
+/* Arrival, first-token and finish times of request id (-1 where not reached yet). */
+pkv_status pkv_sched_request_times(const void* state, int32_t id, double* arrival, double* first_token, double* finish);
+/* Copies up to capacity inter-token gaps (time between consecutive tokens of one request, first
+ * token excluded); returns how many were recorded (-1 on a bad argument). */
+int64_t pkv_sched_itl(const void* state, double* out, int64_t capacity);
+
+/*
  * Fused mixed-batch step ([vLLM-internals], scheduler-loop section: one step carries the decode
  * tokens and the prefill chunks through one forward call; [Chunked-Prefill], token-budget section).
  * One attention launch (plus the decode's plan pass and, for long contexts, its split reduce) that

@@ -56,6 +56,15 @@ _SIGS = {
                                     _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _f32, _f32, _i32, _i32, _vp, _sz,
                                     _vp, _vp]),
     "pkv_compose_step": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_sched_state_bytes": (_sz, [_i32, _i32, _i32, _i64]),
+    "pkv_sched_init": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _vp]),
+    "pkv_sched_add_request": (_i32, [_vp, _i32, _i32, ctypes.c_double, _vp]),
+    "pkv_sched_plan": (_i32, [_vp, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_sched_complete": (_i32, [_vp, ctypes.c_double]),
+    "pkv_sched_table": (_vp, [_vp]),
+    "pkv_sched_num_done": (_i32, [_vp]),
+    "pkv_sched_request_times": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "pkv_sched_itl": (_i64, [_vp, _vp, _i64]),
     "pkv_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_bm_state_bytes": (_sz, [_i32]),
@@ -289,6 +298,77 @@ class BlockManager:
 
     def block_hash(self, block: int) -> int:
         return int(_lib.pkv_bm_block_hash(self._sp(), int(block)))
+
+
+SCHED_NAIVE, SCHED_STATIC, SCHED_CONTINUOUS, SCHED_CHUNKED = 0, 1, 2, 3
+
+
+class Scheduler:
+    """Iteration-level scheduler over synthetic requests (see the pkv_sched_* calls); host code.
+    Block-table rows come from `block_manager` (a BlockManager over the pool the kernels use)."""
+
+    def __init__(self, mode: int, max_requests: int, max_running: int, max_blocks: int, block_manager: BlockManager,
+                 token_budget: int = 0, max_chunk: int = 0, max_itl_samples: int = 1 << 20):
+        import numpy as np
+        self._np = np
+        n = int(_lib.pkv_sched_state_bytes(max_requests, max_running, max_blocks, max_itl_samples))
+        if n == 0:
+            raise ValueError("bad scheduler sizes")
+        self._state = np.zeros((n + 7) // 8, dtype=np.uint64)
+        self._bm = block_manager  # kept alive: the scheduler holds a pointer to its state
+        self.max_running, self.max_blocks = max_running, max_blocks
+        _check(_lib.pkv_sched_init(self._sp(), n, int(mode), max_requests, max_running, max_blocks, max_itl_samples,
+                                   int(token_budget), int(max_chunk), block_manager._sp()), "pkv_sched_init")
+        ptr = _lib.pkv_sched_table(self._sp())
+        self.table = np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_int32)),
+                                           shape=(max_running, max_blocks))
+        mr = max_running
+        self._out = {k: np.zeros(mr, dtype=np.int32) for k in ("dec_row", "dec_ctx", "chunk_row", "chunk_offset",
+                                                                "chunk_len")}
+
+    def _sp(self):
+        return ctypes.c_void_p(self._state.ctypes.data)
+
+    @staticmethod
+    def _ap(a):
+        return ctypes.c_void_p(a.ctypes.data)
+
+    def add_request(self, prompt_len: int, output_len: int, arrival: float) -> int:
+        rid = ctypes.c_int32(0)
+        _check(_lib.pkv_sched_add_request(self._sp(), int(prompt_len), int(output_len), float(arrival),
+                                          ctypes.byref(rid)), "pkv_sched_add_request")
+        return rid.value
+
+    def plan(self, now: float) -> dict:
+        """The step starting at `now`: decode (row, ctx) and chunk (row, offset, len) arrays."""
+        nd, nc, nxt = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_double(0)
+        o = self._out
+        _check(_lib.pkv_sched_plan(self._sp(), float(now), ctypes.byref(nd), self._ap(o["dec_row"]),
+                                   self._ap(o["dec_ctx"]), ctypes.byref(nc), self._ap(o["chunk_row"]),
+                                   self._ap(o["chunk_offset"]), self._ap(o["chunk_len"]), ctypes.byref(nxt)),
+               "pkv_sched_plan")
+        d, c = nd.value, nc.value
+        return {"dec_row": o["dec_row"][:d].copy(), "dec_ctx": o["dec_ctx"][:d].copy(),
+                "chunk_row": o["chunk_row"][:c].copy(), "chunk_offset": o["chunk_offset"][:c].copy(),
+                "chunk_len": o["chunk_len"][:c].copy(), "next_arrival": nxt.value}
+
+    def complete(self, now: float) -> None:
+        _check(_lib.pkv_sched_complete(self._sp(), float(now)), "pkv_sched_complete")
+
+    def num_done(self) -> int:
+        return int(_lib.pkv_sched_num_done(self._sp()))
+
+    def request_times(self, rid: int):
+        a, f, e = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+        _check(_lib.pkv_sched_request_times(self._sp(), int(rid), ctypes.byref(a), ctypes.byref(f), ctypes.byref(e)),
+               "pkv_sched_request_times")
+        return a.value, f.value, e.value
+
+    def itl(self):
+        n = int(_lib.pkv_sched_itl(self._sp(), None, 0))
+        out = self._np.zeros(max(n, 1), dtype=self._np.float64)
+        _lib.pkv_sched_itl(self._sp(), self._ap(out), n)
+        return out[:n]
 
 
 def paged_gather(key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,

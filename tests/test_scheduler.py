@@ -60,3 +60,199 @@ def test_bad_arguments():
         with pytest.raises(pkv.PagedKVError) as e:
             pkv.compose_step(*args)
         assert e.value.status == pkv.INVALID_ARG
+
+
+# ---- iteration-level scheduler ---------------------------------------------------------------
+
+class ModelScheduler:
+    """Plain statement of the four modes of "Phase 17 · 04 — vLLM serving internals" (scheduler-loop
+    section) and the iteration-level loop of "第2章:推理引擎核心技术" §2.3: release finished requests,
+    admit arrived requests in queue order while a slot and blocks for their whole final length are
+    free, then give each running request a prompt (whole, or a budgeted chunk) or one decode token."""
+
+    def __init__(self, mode, max_running, num_blocks, budget, max_chunk):
+        self.mode, self.max_running, self.free = mode, max_running, num_blocks
+        self.budget, self.max_chunk = budget, max_chunk
+        self.reqs, self.waiting, self.running = [], [], []
+        self.itl = []
+
+    def add(self, prompt, output, arrival):
+        self.reqs.append(dict(prompt=prompt, output=output, arrival=arrival, prefilled=0, gen=0, first=-1.0,
+                              finish=-1.0, last=None, held=0))
+        self.waiting.append(len(self.reqs) - 1)
+
+    @staticmethod
+    def blocks(n):
+        return -(-n // 16)
+
+    def need(self, r):
+        return self.blocks(r["prompt"] + r["output"] - 1)
+
+    def plan(self, now):
+        naive, static, chunked = self.mode == 0, self.mode == 1, self.mode == 3
+        cap = 1 if naive else self.max_running
+        reserved = sum(self.need(self.reqs[i]) - self.reqs[i]["held"] for i in self.running)
+        if not (naive or static) or not self.running:
+            while self.waiting and len(self.running) < cap:
+                r = self.reqs[self.waiting[0]]
+                if r["arrival"] > now or self.free - reserved < self.need(r):
+                    break
+                i = self.waiting.pop(0)
+                r["held"] = self.blocks(r["prompt"])
+                self.free -= r["held"]
+                reserved += self.need(r) - r["held"]
+                self.running.append(i)
+        left = self.budget
+        dec, chunks = [], []
+        for i in self.running:
+            r = self.reqs[i]
+            if r["gen"] == 0 or r["gen"] >= r["output"] or r["prefilled"] < r["prompt"]:
+                continue
+            if chunked:
+                if left == 0:
+                    break
+                left -= 1
+            ctx = r["prompt"] + r["gen"]
+            grow = self.blocks(ctx) - self.blocks(ctx - 1)
+            r["held"] += grow
+            self.free -= grow
+            dec.append((i, ctx))
+        for i in self.running:
+            r = self.reqs[i]
+            if r["prefilled"] == r["prompt"]:
+                continue
+            n = r["prompt"] - r["prefilled"]
+            if chunked:
+                if left == 0:
+                    break
+                n = min(n, left)
+                if self.max_chunk > 0:
+                    n = min(n, self.max_chunk)
+                left -= n
+            chunks.append((i, r["prefilled"], n))
+        self._plan = (dec, chunks)
+        return dec, chunks
+
+    def complete(self, now):
+        dec, chunks = self._plan
+
+        def token(r):
+            if r["gen"] == 0:
+                r["first"] = now
+            else:
+                self.itl.append(now - r["last"])
+            r["last"] = now
+            r["gen"] += 1
+            if r["gen"] == r["output"]:
+                r["finish"] = now
+
+        for i, _ in dec:
+            token(self.reqs[i])
+        for i, off, n in chunks:
+            r = self.reqs[i]
+            r["prefilled"] += n
+            if r["prefilled"] == r["prompt"]:
+                token(r)
+        done = [i for i in self.running if self.reqs[i]["gen"] == self.reqs[i]["output"]]
+        if self.mode != 1 or len(done) == len(self.running):
+            for i in done:
+                self.free += self.reqs[i]["held"]
+                self.running.remove(i)
+
+
+def _drive(sched, n, step_time):
+    now, steps = 0.0, 0
+    while sched.num_done() < n:
+        plan = sched.plan(now)
+        if len(plan["dec_row"]) + len(plan["chunk_row"]) == 0:
+            assert plan["next_arrival"] > now
+            now = plan["next_arrival"]
+            continue
+        now += step_time(plan)
+        sched.complete(now)
+        steps += 1
+        assert steps < 100000
+    return steps
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_scheduler_matches_the_model(mode):
+    import paged_kv_cache_170_amd as pkv
+    rng = random.Random(10 + mode)
+    n, nblk, max_run, max_blocks = 40, 400, 6, 64
+    reqs = []
+    t = 0.0
+    for _ in range(n):
+        t += rng.choice([0.0, 0.0, 3.0, 17.5])
+        reqs.append((rng.randint(1, 500), rng.randint(1, 40), t))
+    bm = pkv.BlockManager(nblk)
+    lib = pkv.Scheduler(mode, n, max_run, max_blocks, bm, token_budget=256, max_chunk=96)
+    mod = ModelScheduler(mode, max_run, nblk, 256, 96)
+    for p, o, a in reqs:
+        lib.add_request(p, o, a)
+        mod.add(p, o, a)
+    row_of = {}
+
+    def step_time(plan):
+        return 1.0 + (len(plan["dec_row"]) + int(plan["chunk_len"].sum())) / 64.0
+
+    now = 0.0
+    while lib.num_done() < n:
+        plan = lib.plan(now)
+        dec, chunks = mod.plan(now)
+        assert len(plan["dec_row"]) == len(dec) and len(plan["chunk_row"]) == len(chunks)
+        assert list(plan["dec_ctx"]) == [c for _, c in dec]
+        assert [(int(o), int(l)) for o, l in zip(plan["chunk_offset"], plan["chunk_len"])] == \
+            [(o, l) for _, o, l in chunks]
+        # Rows stay with their request while it runs; the table holds its blocks.
+        for (i, _), row in zip(dec, plan["dec_row"]):
+            assert row_of.setdefault(i, row) == row
+        for (i, _, _), row in zip(chunks, plan["chunk_row"]):
+            assert row_of.setdefault(i, row) == row
+        if not dec and not chunks:
+            now = plan["next_arrival"]
+            continue
+        if mode == 0:
+            assert len(dec) + len(chunks) == 1
+        now += step_time(plan)
+        lib.complete(now)
+        mod.complete(now)
+        for i in [i for i in row_of if mod.reqs[i]["gen"] == mod.reqs[i]["output"] and i not in mod.running]:
+            del row_of[i]
+        assert bm.num_free() == mod.free
+    for i in range(n):
+        a, f, e = lib.request_times(i)
+        r = mod.reqs[i]
+        assert (a, f, e) == (r["arrival"], r["first"], r["finish"])
+        assert f >= a and e >= f
+    assert np.allclose(lib.itl(), mod.itl)
+    assert bm.num_free() == nblk
+
+
+def test_scheduler_modes_order_and_chunking():
+    """Mode differences on one burst of requests: NAIVE runs them one by one, STATIC waits for its
+    whole batch, CHUNKED never exceeds the token budget while CONTINUOUS prefills whole prompts."""
+    import paged_kv_cache_170_amd as pkv
+    reqs = [(300, 5, 0.0), (40, 30, 0.0), (200, 3, 0.0), (500, 8, 0.0)]
+    ttft = {}
+    for mode in range(4):
+        bm = pkv.BlockManager(500)
+        sc = pkv.Scheduler(mode, 4, 4, 64, bm, token_budget=128)
+        for p, o, a in reqs:
+            sc.add_request(p, o, a)
+        biggest = 0
+        now = 0.0
+        while sc.num_done() < 4:
+            plan = sc.plan(now)
+            biggest = max(biggest, len(plan["dec_row"]) + int(plan["chunk_len"].sum()))
+            now += 1.0
+            sc.complete(now)
+        ttft[mode] = [sc.request_times(i)[1] for i in range(4)]
+        if mode == 3:
+            assert biggest <= 128
+        if mode == 2:
+            assert biggest == 300 + 40 + 200 + 500
+    assert ttft[0] == [1.0, 6.0, 36.0, 39.0]     # one request at a time: 1 + 5, + 30, + 3 steps
+    assert ttft[1] == [1.0, 1.0, 1.0, 1.0]       # the whole batch prefilled in its first step
+    assert ttft[2] == [1.0, 1.0, 1.0, 1.0]
+    assert ttft[3][1] < ttft[3][0] or ttft[3][0] > 1.0  # prompts spread over budgeted steps
