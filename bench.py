@@ -55,10 +55,16 @@ def parse():
 
 
 def sources_hash(names):
+    """Hash of a kernel's sources: the .hip file, its device header (if any) and common.hpp."""
     h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_170_amd", "csrc")
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_170_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        for f_name in (n, n.replace(".hip", "_dev.hpp")):
+            path = os.path.join(csrc, f_name)
+            if f_name != n and not os.path.exists(path):
+                continue
+            with open(path, "rb") as f:
+                h.update(f.read())
     with open(os.path.join(ROOT, "paged_kv_cache_170_amd", "csrc", "common.hpp"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
