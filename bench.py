@@ -189,6 +189,7 @@ def main():
         p_cu, p_off, p_bt = to_dev(pre.cu_q_lens), to_dev(pre.chunk_offsets), to_dev(pre.block_tables)
         p_out = torch.empty((pre.query.shape[0], pre.num_q_heads, pre.head_dim), dtype=torch.float32, device=dev)
         p_maxl = int(np.diff(pre.cu_q_lens).max())
+        p_ws = pkv.prefill_workspace(p_q, len(pre.chunk_offsets), p_maxl, pre.max_blocks_per_seq)
     torch.cuda.synchronize()
 
     if args.calib_copy_mib:
@@ -227,10 +228,10 @@ def main():
         if pre is not None:
             if fp8:
                 pkv.paged_attn_prefill_chunk_fp8(p_q, p_cu, p_off, kp8, vp8, p_bt, p_maxl, pre.scale, k_scale, v_scale,
-                                                 causal=True, out=p_out)
+                                                 causal=True, out=p_out, workspace=p_ws)
             else:
                 pkv.paged_attn_prefill_chunk(p_q, p_cu, p_off, kp, vp, p_bt, p_maxl, pre.scale, causal=True,
-                                             out=p_out)
+                                             out=p_out, workspace=p_ws)
         mark(4)
 
     for _ in range(args.warmup):
@@ -293,18 +294,18 @@ def main():
             pkv.paged_attn_mixed(fkp, fvp, dec.scale, dec_query=d_q, dec_block_tables=d_bt, context_lens=d_ctx,
                                  pre_query=p_q, cu_q_lens=p_cu, chunk_offsets=p_off, pre_block_tables=p_bt,
                                  max_q_len=p_maxl, causal=True, k_scale=sc[0], v_scale=sc[1], dec_out=d_out,
-                                 pre_out=p_out, workspace=ws)
+                                 pre_out=p_out, workspace=ws, pre_workspace=p_ws)
 
         def separate():
             if fp8:
                 pkv.paged_attn_decode_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, out=d_out,
                                           workspace=ws)
                 pkv.paged_attn_prefill_chunk_fp8(p_q, p_cu, p_off, kp8, vp8, p_bt, p_maxl, pre.scale, k_scale,
-                                                 v_scale, causal=True, out=p_out)
+                                                 v_scale, causal=True, out=p_out, workspace=p_ws)
             else:
                 pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=d_out, workspace=ws)
                 pkv.paged_attn_prefill_chunk(p_q, p_cu, p_off, kp, vp, p_bt, p_maxl, pre.scale, causal=True,
-                                             out=p_out)
+                                             out=p_out, workspace=p_ws)
 
         times = {}
         for name, fn in (("separate", separate), ("fused", fused), ("separate", separate), ("fused", fused)):

@@ -191,13 +191,26 @@ pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* que
  *   chunk_offsets       int32 [num_seqs] (device), >= 0
  *   max_q_len           host upper bound of L_s (sizes the grid; rows beyond it are not computed)
  *   scale               > 0 (the usual 1/sqrt(head_dim)); other values are PKV_ERR_INVALID_ARG
+ *   workspace           device scratch of >= pkv_prefill_workspace_bytes(...) bytes (16-byte aligned;
+ *                       may be NULL when that is 0); PKV_ERR_WORKSPACE_TOO_SMALL otherwise
  */
 pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* query, const int32_t* cu_q_lens,
                                         const int32_t* chunk_offsets, const void* key_pool, const void* value_pool,
                                         const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
                                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t num_blocks, int32_t causal, float scale,
-                                        pkv_dtype dtype, int32_t* err_flag, void* stream);
+                                        pkv_dtype dtype, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                        void* stream);
+
+/*
+ * Workspace bytes the chunked-prefill calls need for these shapes: when there are fewer 256-row
+ * tiles than compute units, each tile's key range is split over several workgroups whose fp32
+ * partial rows, (max, normaliser) pairs and arrival counters live here.  0 when no split is made
+ * (the workspace may then be NULL).  The calls clear the counters themselves; the contents on
+ * entry are ignored.  A workspace must not be shared by calls that run concurrently.
+ */
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq);
 
 /*
  * FP8 KV pool.  The pages run their model in FP8 ([vLLM-internals], opening benchmark and memory
@@ -245,7 +258,8 @@ pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_dtype, cons
                                             int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
                                             int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                                             int32_t causal, float scale, float k_scale, float v_scale,
-                                            int32_t* err_flag, void* stream);
+                                            void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                            void* stream);
 
 /*
  * Token-budget step composer (host code; [Chunked-Prefill], token-budget section: each step adds one
@@ -325,6 +339,7 @@ int64_t pkv_sched_itl(const void* state, double* out, int64_t capacity);
  *                 chunk_offsets, pre_block_tables [num_pre_seqs, pre_max_blocks], max_q_len, causal
  *   dtype         BF16 pools, or FP8_E4M3 pools with k_scale / v_scale (ignored for BF16); queries bf16
  *   split_tokens, workspace  as for pkv_paged_attn_decode with the decode part's shapes
+ *   pre_workspace       as the workspace of pkv_paged_attn_prefill_chunk for the prefill part
  * head_dim 64 or 128 (a decode workgroup runs two decode workers side by side); 256 is
  * PKV_ERR_UNSUPPORTED.
  */
@@ -336,8 +351,8 @@ pkv_status pkv_paged_attn_mixed(void* dec_out, const void* dec_query, const int3
                                 const void* key_pool, const void* value_pool, int32_t num_blocks,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
                                 pkv_dtype dtype, float k_scale, float v_scale, pkv_dtype out_dtype,
-                                int32_t split_tokens, void* workspace, size_t workspace_bytes, int32_t* err_flag,
-                                void* stream);
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                void* pre_workspace, size_t pre_workspace_bytes, int32_t* err_flag, void* stream);
 
 /*
  * Block copy for copy-on-write ([Engine-core] §1.5; [C13-L2] 改进二, sharing paragraph): for each

@@ -45,16 +45,17 @@ _SIGS = {
     "pkv_paged_attn_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                      _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                            _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
+                                            _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_cache_write_fp8": (_i32, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                    _f32, _vp, _vp]),
     "pkv_paged_attn_decode_fp8": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                          _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk_fp8": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                                _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _vp]),
+                                                _i32, _i32, _i32, _i32, _f32, _f32, _f32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_mixed": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _f32, _f32, _i32, _i32, _vp, _sz,
-                                    _vp, _vp]),
+                                    _vp, _sz, _vp, _vp]),
     "pkv_compose_step": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp]),
     "pkv_sched_state_bytes": (_sz, [_i32, _i32, _i32, _i64]),
     "pkv_sched_init": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _vp]),
@@ -463,13 +464,28 @@ def paged_attn_decode_fp8(query: torch.Tensor, key_pool: torch.Tensor, value_poo
     return out
 
 
+def prefill_workspace_bytes(num_seqs: int, max_q_len: int, num_q_heads: int, head_dim: int,
+                            max_blocks_per_seq: int) -> int:
+    return int(_lib.pkv_prefill_workspace_bytes(num_seqs, max_q_len, num_q_heads, head_dim, max_blocks_per_seq))
+
+
+def prefill_workspace(query: torch.Tensor, num_seqs: int, max_q_len: int, max_blocks_per_seq: int):
+    """Allocate the chunked-prefill workspace for these shapes (None when none is needed)."""
+    n = prefill_workspace_bytes(num_seqs, max_q_len, query.shape[1], query.shape[2], max_blocks_per_seq)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def _ws_args(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
 def paged_attn_prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk_offsets: torch.Tensor,
                              key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,
                              max_q_len: int, scale: float, causal: bool = True, out: torch.Tensor | None = None,
-                             out_dtype: torch.dtype = torch.float32,
+                             out_dtype: torch.dtype = torch.float32, workspace: torch.Tensor | None = None,
                              err_flag: torch.Tensor | None = None) -> torch.Tensor:
     """Chunked-prefill attention over the paged cache; see pkv_paged_attn_prefill_chunk."""
-    _need_gpu(query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables, out, err_flag)
+    _need_gpu(query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables, out, workspace, err_flag)
     _need_i32(cu_q_lens, chunk_offsets, block_tables, err_flag)
     nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
     if query.dim() != 3 or query.shape[2] != hd or query.dtype != key_pool.dtype or not query.is_contiguous():
@@ -482,11 +498,13 @@ def paged_attn_prefill_chunk(query: torch.Tensor, cu_q_lens: torch.Tensor, chunk
         out = torch.empty((rows, hq, hd), dtype=out_dtype, device=query.device)
     elif not out.is_contiguous() or tuple(out.shape) != (rows, hq, hd):
         raise ValueError("out must be contiguous [rows, num_q_heads, head_dim]")
+    if workspace is None:
+        workspace = prefill_workspace(query, num_seqs, int(max_q_len), block_tables.shape[1])
     _check(_lib.pkv_paged_attn_prefill_chunk(_ptr(out), _dtype_code(out), _ptr(query), _ptr(cu_q_lens),
                                              _ptr(chunk_offsets), _ptr(key_pool), _ptr(value_pool),
                                              _ptr(block_tables), block_tables.shape[1], num_seqs, int(max_q_len), hq,
                                              hkv, hd, nblk, int(bool(causal)), float(scale), _dtype_code(key_pool),
-                                             _ptr(err_flag), _stream(query.device)),
+                                             *_ws_args(workspace), _ptr(err_flag), _stream(query.device)),
            "pkv_paged_attn_prefill_chunk")
     return out
 
@@ -495,6 +513,7 @@ def paged_attn_prefill_chunk_fp8(query: torch.Tensor, cu_q_lens: torch.Tensor, c
                                  key_pool: torch.Tensor, value_pool: torch.Tensor, block_tables: torch.Tensor,
                                  max_q_len: int, scale: float, k_scale: float, v_scale: float, causal: bool = True,
                                  out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                                 workspace: torch.Tensor | None = None,
                                  err_flag: torch.Tensor | None = None) -> torch.Tensor:
     """Chunked-prefill attention over E4M3 pools with per-pool scales; see
     pkv_paged_attn_prefill_chunk_fp8."""
@@ -511,11 +530,13 @@ def paged_attn_prefill_chunk_fp8(query: torch.Tensor, cu_q_lens: torch.Tensor, c
         out = torch.empty((rows, hq, hd), dtype=out_dtype, device=query.device)
     elif not out.is_contiguous() or tuple(out.shape) != (rows, hq, hd):
         raise ValueError("out must be contiguous [rows, num_q_heads, head_dim]")
+    if workspace is None:
+        workspace = prefill_workspace(query, num_seqs, int(max_q_len), block_tables.shape[1])
     _check(_lib.pkv_paged_attn_prefill_chunk_fp8(_ptr(out), _dtype_code(out), _ptr(query), _ptr(cu_q_lens),
                                                  _ptr(chunk_offsets), _ptr(key_pool), _ptr(value_pool),
                                                  _ptr(block_tables), block_tables.shape[1], num_seqs,
                                                  int(max_q_len), hq, hkv, hd, nblk, int(bool(causal)), float(scale),
-                                                 float(k_scale), float(v_scale), _ptr(err_flag),
+                                                 float(k_scale), float(v_scale), *_ws_args(workspace), _ptr(err_flag),
                                                  _stream(query.device)), "pkv_paged_attn_prefill_chunk_fp8")
     return out
 
@@ -527,8 +548,8 @@ def paged_attn_mixed(key_pool: torch.Tensor, value_pool: torch.Tensor, scale: fl
                      pre_block_tables: torch.Tensor | None = None, max_q_len: int = 0, causal: bool = True,
                      k_scale: float = 1.0, v_scale: float = 1.0, dec_out: torch.Tensor | None = None,
                      pre_out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-                     workspace: torch.Tensor | None = None, split_tokens: int = 0,
-                     err_flag: torch.Tensor | None = None):
+                     workspace: torch.Tensor | None = None, pre_workspace: torch.Tensor | None = None,
+                     split_tokens: int = 0, err_flag: torch.Tensor | None = None):
     """Decode tokens and prefill chunks of one step in one fused launch; see pkv_paged_attn_mixed.
     Returns (decode output or None, prefill output or None).  bf16 or E4M3 pools (with scales)."""
     _need_gpu(key_pool, value_pool, dec_query, dec_block_tables, context_lens, pre_query, cu_q_lens, chunk_offsets,
@@ -564,6 +585,8 @@ def paged_attn_mixed(key_pool: torch.Tensor, value_pool: torch.Tensor, scale: fl
             raise ValueError("prefill batch sizes differ")
         if pre_out is None:
             pre_out = torch.empty((pre_query.shape[0], hq, hd), dtype=out_dtype, device=pre_query.device)
+        if pre_workspace is None:
+            pre_workspace = prefill_workspace(pre_query, npre, int(max_q_len), pre_block_tables.shape[1])
     if hq is None:
         return None, None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -574,8 +597,8 @@ def paged_attn_mixed(key_pool: torch.Tensor, value_pool: torch.Tensor, scale: fl
                                      _ptr(pre_block_tables), 0 if pre_block_tables is None else pre_block_tables.shape[1],
                                      npre, int(max_q_len), int(bool(causal)), _ptr(key_pool), _ptr(value_pool), nblk, hq,
                                      hkv, hd, float(scale), code, float(k_scale), float(v_scale), out_code,
-                                     int(split_tokens), _ptr(workspace), ws_bytes, _ptr(err_flag),
-                                     _stream(key_pool.device)), "pkv_paged_attn_mixed")
+                                     int(split_tokens), _ptr(workspace), ws_bytes, *_ws_args(pre_workspace),
+                                     _ptr(err_flag), _stream(key_pool.device)), "pkv_paged_attn_mixed")
     return dec_out, pre_out
 
 

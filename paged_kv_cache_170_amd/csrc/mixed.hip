@@ -66,7 +66,7 @@ extern "C" pkv_status pkv_paged_attn_mixed(
     int32_t max_q_len, int32_t causal, const void* key_pool, const void* value_pool, int32_t num_blocks,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale, pkv_dtype dtype, float k_scale,
     float v_scale, pkv_dtype out_dtype, int32_t split_tokens, void* workspace, size_t workspace_bytes,
-    int32_t* err_flag, void* stream) {
+    void* pre_workspace, size_t pre_workspace_bytes, int32_t* err_flag, void* stream) {
   const bool kv8 = dtype == PKV_DTYPE_FP8_E4M3;
   if (dtype != PKV_DTYPE_BF16 && !kv8) return PKV_ERR_UNSUPPORTED;
   if (kv8 && (!scale_ok(k_scale) || !scale_ok(v_scale))) return PKV_ERR_INVALID_ARG;
@@ -135,17 +135,27 @@ extern "C" pkv_status pkv_paged_attn_mixed(
     if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
   }
 
-  // Prefill part: the items of pkv_paged_attn_prefill_chunk.
+  // Prefill part: the items (row tiles x key splits) of pkv_paged_attn_prefill_chunk.
   int pre_items = 0;
+  int64_t pre_row_items = 0;
   PreArgs pa{};
   if (has_pre) {
     const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
-    const int64_t items = static_cast<int64_t>(num_pre_seqs) * num_q_heads * q_tiles;
+    const int64_t row_items = static_cast<int64_t>(num_pre_seqs) * num_q_heads * q_tiles;
+    const int ksplit = pkv_pre::ksplit_for(row_items, pre_max_blocks, head_dim, pkv_host::cu_count());
+    const int64_t items = row_items * ksplit;
     if (items + dec_wgs > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+    const pkv_pre::Layout lay = pkv_pre::layout(row_items, ksplit, head_dim);
+    if (ksplit > 1 && (!pre_workspace || pre_workspace_bytes < lay.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    if (ksplit > 1 && reinterpret_cast<uintptr_t>(pre_workspace) % 16 != 0) return PKV_ERR_INVALID_ARG;
+    char* pw = static_cast<char*>(pre_workspace);
     pre_items = static_cast<int>(items);
     pa = PreArgs{static_cast<const uint16_t*>(pre_query), cu_q_lens, chunk_offsets, key_pool, value_pool,
                  pre_block_tables, pre_max_blocks, q_tiles, num_q_heads, num_kv_heads, group, num_blocks,
-                 causal != 0, scale_log2, vs, pre_out, ob, err_flag};
+                 causal != 0, scale_log2, vs, pre_out, ob, err_flag, ksplit,
+                 ksplit > 1 ? reinterpret_cast<float*>(pw + lay.o) : nullptr,
+                 ksplit > 1 ? reinterpret_cast<float*>(pw + lay.ml) : nullptr};
+    pre_row_items = row_items;
   }
 
   const unsigned grid = static_cast<unsigned>(dec_wgs + pre_items);
@@ -167,6 +177,10 @@ extern "C" pkv_status pkv_paged_attn_mixed(
   if (has_dec && max_splits > 1) {
     launch_reduce(ws_o, ws_ml, context_lens, dec_max_blocks, num_dec_seqs, num_q_heads, num_kv_heads, head_dim, S,
                   max_splits, dec_out, ob, st);
+    if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+  }
+  if (has_pre && pa.ksplit > 1) {
+    pkv_pre::launch_merge(pa, pre_row_items, head_dim, st);
     return pkv_host::launch_status();
   }
   return PKV_OK;

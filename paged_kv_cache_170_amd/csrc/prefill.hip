@@ -30,6 +30,69 @@
 
 namespace pkv {
 
+// Log-sum-exp merge of a row tile's key splits: grid = (row items, kPreTile / 32), 256 threads per
+// 32-row slice.  First 32 threads turn their row's (m, l) pairs into split weights (in split order,
+// so the result does not depend on which split finished first); then the threads sweep the slice's
+// partial rows with 16-byte loads, consecutive threads on consecutive columns of one row.
+constexpr int kMergeRows = 32;
+
+template <int HD>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PreArgs a) {
+  __shared__ float wgt[kMergeRows][kPreMaxSplit];
+  __shared__ float inv_s[kMergeRows];
+  const int w = blockIdx.x, r0 = blockIdx.y * kMergeRows;
+  const int t = w % a.q_tiles;
+  int q = w / a.q_tiles;
+  const int hi = q % a.group;
+  q /= a.group;
+  const int g = q % a.num_kv_heads;
+  const int s = q / a.num_kv_heads;
+  const int h = g * a.group + hi;
+  const int qlo = a.cu_q_lens[s];
+  const int L = a.cu_q_lens[s + 1] - qlo;
+  const int rows = min(kMergeRows, L - t * kPreTile - r0);
+  if (rows <= 0) return;
+  const int ks = a.ksplit;
+  const int64_t base = static_cast<int64_t>(w) * ks * kPreTile + r0;
+  if (threadIdx.x < kMergeRows) {
+    const int r = threadIdx.x;
+    float M = -INFINITY;
+    for (int k = 0; k < ks; ++k) M = fmaxf(M, a.ws_ml[(base + static_cast<int64_t>(k) * kPreTile + r) * 2]);
+    float Ls = 0.f;
+    for (int k = 0; k < ks; ++k) {
+      const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (base + static_cast<int64_t>(k) * kPreTile + r) * 2);
+      const float f = (ml.x == -INFINITY) ? 0.f : fast_exp2(ml.x - M);
+      wgt[r][k] = f;
+      Ls += f * ml.y;
+    }
+    inv_s[r] = Ls > 0.f ? a.v_scale / Ls : 0.f;
+  }
+  __syncthreads();
+  constexpr int Q = HD / 4;  // 16-byte pieces per row
+  for (int i = threadIdx.x; i < rows * Q; i += 256) {
+    const int r = i / Q, d = (i % Q) * 4;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < ks; ++k) {
+      const float f = wgt[r][k];
+      const float4 p = *reinterpret_cast<const float4*>(a.ws_o + (base + static_cast<int64_t>(k) * kPreTile + r) * HD + d);
+      o.x += f * p.x;
+      o.y += f * p.y;
+      o.z += f * p.z;
+      o.w += f * p.w;
+    }
+    const float inv = inv_s[r];
+    o.x *= inv;
+    o.y *= inv;
+    o.z *= inv;
+    o.w *= inv;
+    const int64_t oi = (static_cast<int64_t>(qlo + t * kPreTile + r0 + r) * a.num_q_heads + h) * HD + d;
+    if (a.out_bf16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = uint2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + oi) = o;
+  }
+}
+
 template <int HD, bool CHECK, bool NARROW, bool KV8>
 __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(PreArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[PreCfg<HD>::LDS];
@@ -41,6 +104,16 @@ __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(PreArgs a) {
 
 using namespace pkv;
 
+void pkv_pre::launch_merge(const PreArgs& a, int64_t row_items, int32_t head_dim, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(row_items), kPreTile / kMergeRows);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, grid, dim3(kPreTile), 0, st, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, grid, dim3(kPreTile), 0, st, a);
+  else
+    hipLaunchKernelGGL(prefill_merge_kernel<256>, grid, dim3(kPreTile), 0, st, a);
+}
+
 namespace {
 
 // Shared body of the bf16 and FP8 prefill calls (dtype = pool dtype; queries are bf16).
@@ -49,7 +122,7 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
                         const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_q_len,
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                         int32_t causal, float scale, pkv_dtype dtype, float k_scale, float v_scale,
-                        int32_t* err_flag, void* stream) {
+                        void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
   const bool kv8 = dtype == PKV_DTYPE_FP8_E4M3;
   if (kv8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f)))
     return PKV_ERR_INVALID_ARG;
@@ -67,8 +140,14 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
   for (const void* p : {static_cast<const void*>(out), query, key_pool, value_pool})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARG;
   const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
-  const int64_t items = static_cast<int64_t>(num_seqs) * num_q_heads * q_tiles;
+  const int64_t row_items = static_cast<int64_t>(num_seqs) * num_q_heads * q_tiles;
+  const int ksplit = pkv_pre::ksplit_for(row_items, max_blocks_per_seq, head_dim, pkv_host::cu_count());
+  const int64_t items = row_items * ksplit;
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  const pkv_pre::Layout lay = pkv_pre::layout(row_items, ksplit, head_dim);
+  if (ksplit > 1 && (!workspace || workspace_bytes < lay.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (ksplit > 1 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PKV_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
   const int group = num_q_heads / num_kv_heads;
   const float scale_log2 = kv8 ? scale * kLog2e * k_scale : scale * kLog2e;
   const float vs = kv8 ? v_scale : 1.f;
@@ -79,7 +158,9 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
                       num_blocks < (1 << 24);
   const PreArgs pa{static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
                    max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks, causal != 0,
-                   scale_log2, vs, out, ob, err_flag};
+                   scale_log2, vs, out, ob, err_flag, ksplit,
+                   ksplit > 1 ? reinterpret_cast<float*>(ws + lay.o) : nullptr,
+                   ksplit > 1 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr};
 #define PKV_PRE(HD, CHECK, NARROW, KV8)                                                                  \
   hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK, NARROW, KV8>), dim3(static_cast<unsigned>(items)), \
                      dim3(kPreThreads), 0, st, pa)
@@ -98,7 +179,12 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
 #undef PKV_PRE_N
 #undef PKV_PRE_K
 #undef PKV_PRE
-  return pkv_host::launch_status();
+  if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+  if (ksplit > 1) {
+    pkv_pre::launch_merge(pa, row_items, head_dim, st);
+    return pkv_host::launch_status();
+  }
+  return PKV_OK;
 }
 
 }  // namespace
@@ -109,12 +195,22 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtyp
                                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
                                                    int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
                                                    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-                                                   int32_t causal, float scale, pkv_dtype dtype, int32_t* err_flag,
-                                                   void* stream) {
+                                                   int32_t causal, float scale, pkv_dtype dtype, void* workspace,
+                                                   size_t workspace_bytes, int32_t* err_flag, void* stream) {
   if (dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // FP8 pools need their scales
   return prefill_impl(out, out_dtype, query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
                       max_blocks_per_seq, num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, causal,
-                      scale, dtype, 1.f, 1.f, err_flag, stream);
+                      scale, dtype, 1.f, 1.f, workspace, workspace_bytes, err_flag, stream);
+}
+
+extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq) {
+  if (num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+      (head_dim != 64 && head_dim != 128 && head_dim != 256))
+    return 0;
+  const int64_t row_items = static_cast<int64_t>(num_seqs) * num_q_heads * ((max_q_len + kPreTile - 1) / kPreTile);
+  const int ksplit = pkv_pre::ksplit_for(row_items, max_blocks_per_seq, head_dim, pkv_host::cu_count());
+  return pkv_pre::layout(row_items, ksplit, head_dim).total;
 }
 
 extern "C" pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_dtype, const void* query,
@@ -124,8 +220,9 @@ extern "C" pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_
                                                        int32_t num_seqs, int32_t max_q_len, int32_t num_q_heads,
                                                        int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                                                        int32_t causal, float scale, float k_scale, float v_scale,
-                                                       int32_t* err_flag, void* stream) {
+                                                       void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                                                       void* stream) {
   return prefill_impl(out, out_dtype, query, cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
                       max_blocks_per_seq, num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, num_blocks, causal,
-                      scale, PKV_DTYPE_FP8_E4M3, k_scale, v_scale, err_flag, stream);
+                      scale, PKV_DTYPE_FP8_E4M3, k_scale, v_scale, workspace, workspace_bytes, err_flag, stream);
 }

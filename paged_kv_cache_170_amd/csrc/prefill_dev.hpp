@@ -9,10 +9,11 @@
 namespace pkv {
 
 
-constexpr int kPreWaves = 8;                    // two groups of four waves
+constexpr int kPreWaves = 8;                    // eight row waves sharing every key tile
 constexpr int kPreThreads = kPreWaves * kWave;
 constexpr int kPreRows = 32;                    // query rows per wave
-constexpr int kPreTile = 4 * kPreRows;          // query rows per workgroup
+constexpr int kPreTile = kPreWaves * kPreRows;  // query rows per workgroup (256)
+constexpr int kPreMaxSplit = 8;                 // largest number of key splits of one row tile
 constexpr int kIdWindow = 2048;                 // block ids held in LDS (32,768 positions)
 
 // E: bytes per pool element (2 for bf16, 1 for E4M3 codes); LDS tiles are bf16 either way.
@@ -30,8 +31,6 @@ struct PreCfg {
   static constexpr int TILE = KT * (KPITCH + VPITCH);
   static constexpr int LOADS = 2 * KT * CPR / kPreThreads;  // chunks per thread per tensor per tile pair
   static constexpr int LDS = 4 * TILE;                       // two buffers of a tile pair
-  static constexpr int COMB = 4 * kPreRows * HD * 4 + 2 * 4 * kPreRows * 4;
-  static_assert(LDS >= COMB, "merge area must fit in the tile buffers");
   static_assert(LOADS * kPreThreads == 2 * KT * CPR, "pair loads must divide evenly");
 };
 
@@ -51,12 +50,19 @@ struct PreArgs {
   void* out;
   int out_bf16;
   int32_t* err_flag;
+  // Key split: the key range of a row tile is cut into ksplit runs of whole tile pairs, one per
+  // workgroup; with ksplit > 1 each writes its (o, m, l) partial to ws_o / ws_ml and
+  // prefill_merge_kernel writes the output.
+  int ksplit;
+  float* ws_o;   // [row items][ksplit][kPreTile][HD]
+  float* ws_ml;  // [row items][ksplit][kPreTile][2]
 };
 
-// One work item (128 query rows of one query head) on a 512-thread workgroup.  id / items: the
-// item's index among `items` consecutive workgroups (the remap below assumes workgroups are dealt
-// round-robin over the 8 XCDs starting at an XCD boundary).  smem holds PreCfg<HD>::LDS bytes and
-// ids kIdWindow ints (the block ids of logical blocks [win0, win0 + kIdWindow)).
+// One work item (one key split of 256 query rows of one query head) on a 512-thread workgroup.
+// id / items: the item's index among `items` consecutive workgroups (the remap below assumes
+// workgroups are dealt round-robin over the 8 XCDs starting at an XCD boundary, and keeps the
+// splits of a row tile next to each other, on one XCD).  smem holds PreCfg<HD>::LDS bytes and ids
+// kIdWindow ints (the block ids of logical blocks [win0, win0 + kIdWindow)).
 template <int HD, bool CHECK, bool NARROW, bool KV8>
 __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int items, char* smem, int* ids) {
   constexpr int E = KV8 ? 1 : 2;
@@ -75,7 +81,10 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   int32_t* err_flag = A_.err_flag;
 
   // Work item: XCD-contiguous remap of the linear workgroup id.
-  const int w = (items % 8 == 0) ? (id % 8) * (items / 8) + id / 8 : id;
+  const int ksplit = A_.ksplit;
+  const int wk = (items % 8 == 0) ? (id % 8) * (items / 8) + id / 8 : id;
+  const int kh = wk % ksplit;  // key split
+  const int w = wk / ksplit;   // row-tile item
   const int t = w % q_tiles;
   int r = w / q_tiles;
   const int hi = r % group;
@@ -96,9 +105,8 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   const int kv_end = causal ? off + min(row0 + kPreTile, L) : off + L;
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int grp = wave >> 2, wq = wave & 3;  // group grp takes key tiles grp, grp + 2, ...
   const int qc = lane & 31, hh = lane >> 5;
-  const int wrow0 = row0 + wq * kPreRows;
+  const int wrow0 = row0 + wave * kPreRows;
   const int myrow = wrow0 + qc;
   const bool row_ok = myrow < L;
   const int qpos = off + myrow;
@@ -185,31 +193,40 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
     }
   };
 
+  // This split's tile pairs: [p_lo, p_hi) of the row tile's pairs.
   const int ntiles = (kv_end + C::KT - 1) / C::KT;
-  const int npairs = (ntiles + 1) / 2;
-  fill_ids(0);
+  const int npairs_all = (ntiles + 1) / 2;
+  const int per = (npairs_all + ksplit - 1) / ksplit;
+  const int p_lo = min(kh * per, npairs_all), p_hi = min(p_lo + per, npairs_all);
+  constexpr int kPairBlocks = 2 * C::KT / kBlockSize;
+  win0 = p_lo * kPairBlocks;
+  fill_ids(win0);
   __syncthreads();
-  load_pair(0);
-  store_pair(0);
+  if (p_lo < p_hi) {
+    load_pair(p_lo);
+    store_pair(0);
+  }
   __syncthreads();
 
   const int li = lane & 15, dg = (lane >> 4) & 1;
   constexpr int VP = C::VPITCH / 2;
-  constexpr int kPairBlocks = 2 * C::KT / kBlockSize;
-  for (int pr = 0; pr < npairs; ++pr) {
-    const int cur = pr & 1;
-    // Slide the id window when pair pr + 2 (the furthest one read ahead) leaves it.
-    if ((pr + 3) * kPairBlocks - win0 > kIdWindow && (pr + 1) * kPairBlocks < nblk_kv) {
+  for (int pr = p_lo; pr < p_hi; ++pr) {
+    const int cur = (pr - p_lo) & 1;
+    // Slide the id window when pair pr + 1 (the one read ahead) would leave it.
+    if ((pr + 2) * kPairBlocks - win0 > kIdWindow && (pr + 1) * kPairBlocks < nblk_kv) {
       win0 = (pr + 1) * kPairBlocks;
       fill_ids(win0);
       __syncthreads();
     }
-    if (pr + 1 < npairs) load_pair(pr + 1);
-    const int kt = 2 * pr + grp;
+    if (pr + 1 < p_hi) load_pair(pr + 1);
+    // Every wave takes both tiles of the pair (one loop body: unrolling it doubles live registers).
+#pragma unroll 1
+    for (int tt = 0; tt < 2; ++tt) {
+    const int kt = 2 * pr + tt;
     const int key0 = kt * C::KT;
     const bool active = kt < ntiles && wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
     if (active) {
-      const char* tile = smem + (2 * cur + grp) * C::TILE;
+      const char* tile = smem + (2 * cur + tt) * C::TILE;
       floatx16 sacc[C::MS];
       // The MS accumulators are interleaved so that consecutive MFMAs are independent.
 #pragma unroll
@@ -316,56 +333,92 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    if (pr + 1 < npairs) store_pair(cur ^ 1);
+    }
+    if (pr + 1 < p_hi) store_pair(cur ^ 1);
     __syncthreads();
   }
 
-  // Merge the two key groups: group 1 parks its state in LDS, group 0 combines and writes.
+  // Output.  One split: normalise and write.  Several: every split writes its (o, m, l)
+  // partial; the last to arrive merges them with the log-sum-exp rule and writes the rows.
   l_run += __shfl_xor(l_run, 32);
-  float* co = reinterpret_cast<float*>(smem);
-  float* cm = co + 4 * kPreRows * HD;
-  float* cl = cm + 4 * kPreRows;
-  if (grp == 1) {
+  const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
+  auto write_rows = [&](float ia) {
 #pragma unroll
     for (int md = 0; md < C::MD; ++md)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * md + 8 * i + 4 * hh;
-        *reinterpret_cast<float4*>(co + (wq * kPreRows + qc) * HD + d) =
-            float4{acc[md][4 * i], acc[md][4 * i + 1], acc[md][4 * i + 2], acc[md][4 * i + 3]};
+        const float v0 = acc[md][4 * i] * ia, v1 = acc[md][4 * i + 1] * ia, v2 = acc[md][4 * i + 2] * ia,
+                    v3 = acc[md][4 * i + 3] * ia;
+        if (out_bf16) {
+          uint16_t* o = static_cast<uint16_t*>(out) + obase + d;
+          const uint2 pk = uint2{static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
+                                 static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16)};
+          *reinterpret_cast<uint2*>(o) = pk;
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + obase + d) = float4{v0, v1, v2, v3};
+        }
       }
-    if (hh == 0) {
-      cm[wq * kPreRows + qc] = m_ref;
-      cl[wq * kPreRows + qc] = l_run;
-    }
+  };
+  if (HD > 128 || ksplit == 1) {
+    if (!row_ok) return;
+    const float inv = l_run > 0.f ? v_scale / l_run : 0.f;
+    write_rows(inv);
+    return;
   }
-  __syncthreads();
-  if (grp == 1 || !row_ok) return;
-  const float mb = cm[wq * kPreRows + qc], lb = cl[wq * kPreRows + qc];
-  const float M = fmaxf(m_ref, mb);
-  const float fa = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - M);
-  const float fb = (mb == -INFINITY) ? 0.f : fast_exp2(mb - M);
-  const float Ls = fa * l_run + fb * lb;
-  const float inv = Ls > 0.f ? v_scale / Ls : 0.f;
-  const float ia = fa * inv, ib = fb * inv;
-  const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
+  if constexpr (HD <= 128) {
+  // Several splits: write this split's (o, m, l) partial; prefill_merge_kernel combines them
+  // after the launch (the kernel boundary orders the writes before the reads on every XCD).
+  const int prow = wave * kPreRows + qc;  // row inside the tile
+  const int64_t part = (static_cast<int64_t>(w) * ksplit + kh) * kPreTile + prow;
+  float* my_o = A_.ws_o + part * HD;
 #pragma unroll
   for (int md = 0; md < C::MD; ++md)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * md + 8 * i + 4 * hh;
-      const float4 ob = *reinterpret_cast<const float4*>(co + (wq * kPreRows + qc) * HD + d);
-      const float v0 = acc[md][4 * i] * ia + ob.x * ib, v1 = acc[md][4 * i + 1] * ia + ob.y * ib,
-                  v2 = acc[md][4 * i + 2] * ia + ob.z * ib, v3 = acc[md][4 * i + 3] * ia + ob.w * ib;
-      if (out_bf16) {
-        uint16_t* o = static_cast<uint16_t*>(out) + obase + d;
-        const uint2 pk = uint2{static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
-                               static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16)};
-        *reinterpret_cast<uint2*>(o) = pk;
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(out) + obase + d) = float4{v0, v1, v2, v3};
-      }
+      *reinterpret_cast<float4*>(my_o + d) = float4{acc[md][4 * i], acc[md][4 * i + 1], acc[md][4 * i + 2], acc[md][4 * i + 3]};
     }
+  if (hh == 0) *reinterpret_cast<float2*>(A_.ws_ml + part * 2) = float2{m_ref, l_run};
+  }
 }
 
 }  // namespace pkv
+
+// Host helpers shared by the prefill and mixed-step entry points.
+namespace pkv_pre {
+
+// Key splits of a row tile: enough workgroups to give every CU one (each takes a whole CU's LDS),
+// at most kPreMaxSplit, and no more than the tile pairs the longest possible context has.
+inline int ksplit_for(int64_t row_items, int32_t max_blocks, int32_t head_dim, int cus) {
+  // head_dim 256 keeps one split: its registers leave no room for the merge.
+  if (row_items <= 0 || head_dim > 128) return 1;
+  int64_t k = (cus + row_items - 1) / row_items;
+  const int kt = head_dim == 256 ? 32 : 64;
+  const int64_t pairs = (static_cast<int64_t>(max_blocks) * pkv::kBlockSize + 2 * kt - 1) / (2 * kt);
+  if (k > pkv::kPreMaxSplit) k = pkv::kPreMaxSplit;
+  if (k > pairs) k = pairs;
+  return k < 1 ? 1 : static_cast<int>(k);
+}
+
+// Workspace of the key splits: partial rows and their (max, normaliser) pairs, each part on a
+// 256-byte boundary.  Nothing when there is one split.
+struct Layout {
+  size_t o, ml, total;
+};
+
+inline Layout layout(int64_t row_items, int ksplit, int32_t head_dim) {
+  Layout l{0, 0, 0};
+  if (ksplit <= 1) return l;
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = static_cast<size_t>(row_items) * ksplit * pkv::kPreTile;
+  l.o = 0;
+  l.ml = r256(rows * head_dim * 4);
+  l.total = l.ml + r256(rows * 2 * 4);
+  return l;
+}
+
+// Merge the key splits' partials into the output (prefill.hip); a no-op launch is never made.
+void launch_merge(const pkv::PreArgs& a, int64_t row_items, int32_t head_dim, hipStream_t st);
+
+}  // namespace pkv_pre

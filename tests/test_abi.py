@@ -79,10 +79,10 @@ def test_host_validation_rejects_bad_arguments():
     assert dec(null, 0, null, null, null, null, 8, null, 0, 8, 8, 64, 10, 0.1, 1, 0, null, 0, null, null) == 0
     # Prefill: bf16 only, head_dim list, null pointers.
     pre = lib.pkv_paged_attn_prefill_chunk
-    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 0, null, null) == 2
-    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 80, 10, 1, 0.1, 1, null, null) == 2
-    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 1, null, null) == 1
-    assert pre(null, 0, null, null, null, null, null, null, 8, 0, 10, 8, 8, 64, 10, 1, 0.1, 1, null, null) == 0
+    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 0, null, 0, null, null) == 2
+    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 80, 10, 1, 0.1, 1, null, 0, null, null) == 2
+    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 1, null, 0, null, null) == 1
+    assert pre(null, 0, null, null, null, null, null, null, 8, 0, 10, 8, 8, 64, 10, 1, 0.1, 1, null, 0, null, null) == 0
     # Cache write: block size, stride, null pointers, empty.
     cw = lib.pkv_cache_write
     assert cw(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 8, 1, null, null) == 2
@@ -92,7 +92,7 @@ def test_host_validation_rejects_bad_arguments():
     # FP8 pools: the generic calls refuse them (they need scales); the *_fp8 calls check scales,
     # input dtype and pointers before any device work.
     assert dec(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 2, 0, null, 0, null, null) == 2
-    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 2, null, null) == 2
+    assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 2, null, 0, null, null) == 2
     assert cw(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 2, null, null) == 2
     d8 = lib.pkv_paged_attn_decode_fp8
     assert d8(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 0.0, 1.0, 0, null, 0, null, null) == 1
@@ -101,9 +101,9 @@ def test_host_validation_rejects_bad_arguments():
     assert d8(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 1.0, 1.0, 0, null, 0, null, null) == 1
     assert d8(null, 0, null, null, null, null, 8, null, 0, 8, 8, 64, 10, 0.1, 1.0, 1.0, 0, null, 0, null, null) == 0
     p8 = lib.pkv_paged_attn_prefill_chunk_fp8
-    assert p8(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, -1.0, 1.0, null, null) == 1
-    assert p8(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 1.0, 1.0, null, null) == 1
-    assert p8(null, 0, null, null, null, null, null, null, 8, 0, 10, 8, 8, 64, 10, 1, 0.1, 1.0, 1.0, null, null) == 0
+    assert p8(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, -1.0, 1.0, null, 0, null, null) == 1
+    assert p8(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 1.0, 1.0, null, 0, null, null) == 1
+    assert p8(null, 0, null, null, null, null, null, null, 8, 0, 10, 8, 8, 64, 10, 1, 0.1, 1.0, 1.0, null, 0, null, null) == 0
     w8 = lib.pkv_cache_write_fp8
     assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 2, 1.0, 1.0, null, null) == 2  # fp8 input
     assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 1, float("nan"), 1.0, null, null) == 1
