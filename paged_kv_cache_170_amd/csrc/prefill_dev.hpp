@@ -338,8 +338,7 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
     __syncthreads();
   }
 
-  // Output.  One split: normalise and write.  Several: every split writes its (o, m, l)
-  // partial; the last to arrive merges them with the log-sum-exp rule and writes the rows.
+  // Output.  One split: normalise and write the rows.  Several: see below.
   l_run += __shfl_xor(l_run, 32);
   const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
   auto write_rows = [&](float ia) {

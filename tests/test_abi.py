@@ -109,6 +109,14 @@ def test_host_validation_rejects_bad_arguments():
     assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 1, float("nan"), 1.0, null, null) == 1
     assert w8(null, null, 512, 512, null, null, null, 4, 10, 8, 64, 16, 1, 1.0, 1.0, null, null) == 1
     assert w8(null, null, 512, 512, null, null, null, 0, 10, 8, 64, 16, 0, 1.0, 1.0, null, null) == 0
+    # Prefill workspace: none for one key split (many row tiles), some for few row tiles; the call
+    # refuses a missing workspace when one is needed.
+    pwb = lib.pkv_prefill_workspace_bytes
+    assert pwb(1, 512, 64, 128, 2048) > 0 and pwb(64, 4096, 64, 128, 2048) == 0 and pwb(1, 512, 64, 96, 64) == 0
+    assert pwb(1, 512, 4, 256, 2048) == 0  # head_dim 256 never splits
+    fake = ctypes.c_void_p(16)
+    assert pre(fake, 0, fake, fake, fake, fake, fake, fake, 2048, 1, 512, 64, 8, 128, 10, 1, 0.1, 1, null, 0, null,
+               null) == 3
     # Slot mapping.
     sm = lib.pkv_slot_mapping
     assert sm(null, null, 4, null, null, 2, 5, 10, 8, null, null) == 2
