@@ -23,6 +23,9 @@ def command(out_path: str, extra=()) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # Packed fp32 instructions stay off: the compiler emits plain VALU ops instead.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # No wave-level aggregation of atomics: the decode's work-queue fetch is issued by one
+            # lane and its result is read only when the item ends.
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
             *extra, *srcs, "-o", out_path]
 

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 
 // Persistent decode kernel: one worker per workgroup (see decode_worker).
 template <int HD, bool CHECK, bool NARROW, bool KV8>
-__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a, const int2* __restrict__ pieces,
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(HD > 128 ? 1 : 2))) void decode_bf16_kernel(DecArgs a, const int2* __restrict__ pieces,
                                                                   int32_t* __restrict__ plan, int queues) {
   __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
   __shared__ int fetched[2];

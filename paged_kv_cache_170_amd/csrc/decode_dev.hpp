@@ -129,18 +129,22 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   it.my_id[0] = lane < nblk_split ? load_block_id<CHECK>(table, j0 + lane, A_.num_blocks, A_.err_flag) : -1;
   it.my_id[1] = lane + kWave < nblk_split ? load_block_id<CHECK>(table, j0 + kWave + lane, A_.num_blocks, A_.err_flag)
                                           : -1;
-  // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.
-  const bool live = n < A_.group && it.ctx > 0;
-  const uint16_t* qrow =
-      A_.query + (static_cast<int64_t>(it.s) * A_.num_q_heads + it.g * A_.group + (live ? n : 0)) * HD + 8 * c;
+  // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.  Columns
+  // n >= G repeat head G - 1 (their results are never written), so the loads need no select and
+  // nothing waits for them before the first MFMA.
+  const int hn = min(n, A_.group - 1);
+  const uint16_t* qrow = A_.query + (static_cast<int64_t>(it.s) * A_.num_q_heads + it.g * A_.group + hn) * HD + 8 * c;
 #pragma unroll
-  for (int kk = 0; kk < DecCfg<HD>::KK; ++kk) it.qf[kk] = live ? as_bf16x8(ld16(qrow + 32 * kk)) : bf16x8{};
+  for (int kk = 0; kk < DecCfg<HD>::KK; ++kk) it.qf[kk] = as_bf16x8(ld16(qrow + 32 * kk));
 }
 
 // sync: barrier of the 256 threads running the item (the whole workgroup, or one half of a
 // 512-thread workgroup in the fused mixed-step kernel).
-template <int HD, bool CHECK, bool NARROW, bool KV8, class Sync>
-__device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecItem<HD>& it, char* smem, Sync& sync) {
+// on_start: called by every thread once this wave's first gather is issued (the worker fetches
+// its next item there, so those reads queue behind the gather rather than ahead of it).
+template <int HD, bool CHECK, bool NARROW, bool KV8, class Sync, class OnStart>
+__device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecItem<HD>& it, char* smem, Sync& sync,
+                                                 OnStart&& on_start) {
   constexpr int E = KV8 ? 1 : 2;  // pool bytes per element
   using C = DecCfg<HD, E>;
   const int s = it.s, g = it.g, split = it.split, ctx = it.ctx, nsplit = it.nsplit;
@@ -293,8 +297,10 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   };
 
   DecBuf<HD, E> A;
+  if (wave < units) load(wave, A);
+  on_start();
   for (int u = wave; u < units; u += kDecWaves) {
-    load(u, A);
+    if (u != wave) load(u, A);
     compute(u, A);
   }
 
@@ -368,19 +374,25 @@ __device__ __forceinline__ void decode_worker(const DecArgs& a, const int2* __re
   // right after it; the next write to slot p comes after one more barrier.
   for (int p = 0;; p ^= 1) {
     const bool have_next = nxt_i < total;
-    int after = total;
-    if (have_next) {
-      if (tid == 0) after = atomicAdd(&plan[queue * kCounterStride], 1) * queues + queue;  // returns while this item runs
-      find(nxt_i, nxt);
-      decode_item_prologue<HD, CHECK>(a, nxt);  // in flight while this item runs
-    }
+    // Lane 0's old counter value.  It is first read when the item ends, so the atomic's round trip
+    // overlaps the item (this needs the library's build without the atomic optimizer, whose
+    // wave-level aggregation reads the result right away).
+    int ticket = 0;
+    auto fetch_next = [&]() {
+      if (have_next) {
+        if (tid == 0) ticket = atomicAdd(&plan[queue * kCounterStride], 1);
+        find(nxt_i, nxt);
+        decode_item_prologue<HD, CHECK>(a, nxt);  // in flight while this item runs
+      }
+    };
     if (cur.ctx == 0) {
+      fetch_next();
       for (int i = tid; i < a.group * HD; i += kDecThreads)
         store_out(a.out, (static_cast<int64_t>(cur.s) * a.num_q_heads + cur.g * a.group) * HD + i, 0.f, a.out_bf16);
     } else {
-      decode_bf16_item<HD, CHECK, NARROW, KV8>(a, cur, smem, sync);
+      decode_bf16_item<HD, CHECK, NARROW, KV8>(a, cur, smem, sync, fetch_next);
     }
-    if (tid == 0) fetched[p] = after;
+    if (tid == 0) fetched[p] = have_next ? ticket * queues + queue : total;
     sync();  // the next item reuses the staging and merge areas; fetched[p] is published
     if (!have_next) break;
     cur = nxt;
