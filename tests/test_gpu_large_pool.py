@@ -1,0 +1,156 @@
+"""GPU tests of pools larger than 4 GiB (needs an MI355X).
+
+Below 4 GiB per pool the kernels address a block with 32-bit byte offsets; larger pools take the
+64-bit form of the same kernels.  Physical block ids only say where rows live, so moving every
+block of a case to ids past the 4 GiB line must leave every output bit-identical to the same case
+in a small pool (a table maps logical blocks to any physical ones, "第2章:推理引擎核心技术" §1.2).
+The cache write, the decode, the prefill chunk and the fused launch are compared that way, with
+bf16 pools (32 KiB blocks, ids from 132,072) and E4M3 pools (16 KiB blocks, ids from 263,144),
+and the outputs are also checked against the oracle.  Blocks outside the case are never touched,
+so the large pools are left uninitialised.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8 as ofp8
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 1e-2, 1e-3
+HQ, HKV, HD = 64, 8, 128
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_170_amd as m
+    return m
+
+
+def to_dev(a, dev, bf16=False):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+
+def close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, f"{what}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}"
+
+
+def shift_ids(bt, base):
+    """The same table with every used id moved up by base (unused entries stay as they are)."""
+    out = bt.copy()
+    used = bt != wl.UNUSED_BLOCK_ID
+    out[used] += base
+    return out
+
+
+def run_all(pkv, dev, c, dq, kp, vp, bt, num_blocks, fp8):
+    """Cache write of the case's new tokens, then decode, prefill and the fused launch over the
+    same pools and table; returns the outputs on the host."""
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    maxl = int(np.diff(c.new_cu_lens).max())
+    d_bt = to_dev(bt, dev)
+    slots = pkv.slot_mapping(d_bt, to_dev(c.new_cu_lens, dev), to_dev(c.new_start_pos, dev), maxl, num_blocks,
+                             err_flag=err, total=c.num_new_tokens)
+    knew, vnew = to_dev(c.key_new, dev, True), to_dev(c.value_new, dev, True)
+    scales = (0.0123, 2.0 ** -5)
+    if fp8:
+        pkv.cache_write_fp8(knew, vnew, kp, vp, slots, *scales, err_flag=err)
+    else:
+        pkv.cache_write(knew, vnew, kp, vp, slots, err_flag=err)
+    ctx = (c.chunk_offsets + np.diff(c.cu_q_lens)).astype(np.int32)
+    pq, cu, offs = to_dev(c.query, dev, True), to_dev(c.cu_q_lens, dev), to_dev(c.chunk_offsets, dev)
+    dctx = to_dev(ctx, dev)
+    qmax = int(np.diff(c.cu_q_lens).max())
+    if fp8:
+        dec = pkv.paged_attn_decode_fp8(dq, kp, vp, d_bt, dctx, c.scale, *scales, err_flag=err)
+        pre = pkv.paged_attn_prefill_chunk_fp8(pq, cu, offs, kp, vp, d_bt, qmax, c.scale, *scales, causal=True,
+                                               err_flag=err)
+    else:
+        dec = pkv.paged_attn_decode(dq, kp, vp, d_bt, dctx, c.scale, err_flag=err)
+        pre = pkv.paged_attn_prefill_chunk(pq, cu, offs, kp, vp, d_bt, qmax, c.scale, causal=True, err_flag=err)
+    fd, fp = pkv.paged_attn_mixed(kp, vp, c.scale, dec_query=dq, dec_block_tables=d_bt, context_lens=dctx,
+                                  pre_query=pq, cu_q_lens=cu, chunk_offsets=offs, pre_block_tables=d_bt,
+                                  max_q_len=qmax, causal=True, k_scale=scales[0] if fp8 else 1.0,
+                                  v_scale=scales[1] if fp8 else 1.0, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, f"device checks flagged {int(err.item()):#x}"
+    # The case's blocks in logical order (sequence by sequence), as raw bytes.
+    used = torch.from_numpy(bt[bt != wl.UNUSED_BLOCK_ID].astype(np.int64)).to(dev)
+    rows_k = kp.view(torch.uint8).index_select(0, used).cpu()
+    rows_v = vp.view(torch.uint8).index_select(0, used).cpu()
+    host = lambda t: t.cpu().numpy()
+    return host(dec), host(pre), host(fd), host(fp), rows_k, rows_v
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_pools_past_4gib_bit_identical(pkv, fp8):
+    dev = torch.device("cuda:0")
+    elem = 1 if fp8 else 2
+    blk_bytes = 16 * HKV * HD * elem
+    base = (1 << 32) // blk_bytes + 1000  # first id of the case in the large pool
+    c = wl.random_case(4242 + fp8, kind="prefill", dtype="bf16", num_seqs=4, num_q_heads=HQ, num_kv_heads=HKV,
+                       head_dim=HD, max_ctx=2600, q_len_max=300, causal=True, poison=True)
+    nbig = base + c.num_blocks + 16
+    _say(f"case large pool: fp8={fp8} {nbig} blocks of {blk_bytes} B "
+         f"({2 * nbig * blk_bytes / 2**30:.1f} GiB for K and V), ids from {base}")
+    assert nbig * blk_bytes > (1 << 32)
+    rng = np.random.default_rng(7 + fp8)
+    dq_host = wl.f32_to_bf16_bits(rng.standard_normal((4, HQ, HD)).astype(np.float32))
+    dq = to_dev(dq_host, dev, True)
+    # Small pools: the case as generated; large pools: the same blocks at id + base.
+    pool_dtype = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    shape = (c.num_blocks, 16, HKV, HD)
+    k16, v16 = to_dev(c.key_pool, dev, True), to_dev(c.value_pool, dev, True)
+    if fp8:
+        # Both pools hold the quantised case (written by the library's own FP8 write).
+        n = c.num_blocks * 16
+        ks = torch.empty(shape, dtype=pool_dtype, device=dev)
+        vs = torch.empty_like(ks)
+        pkv.cache_write_fp8(k16.view(n, HKV, HD), v16.view(n, HKV, HD), ks, vs,
+                            torch.arange(n, dtype=torch.int32, device=dev), 0.0123, 2.0 ** -5)
+    else:
+        ks, vs = k16, v16
+    kb = torch.empty((nbig, 16, HKV, HD), dtype=pool_dtype, device=dev)
+    vb = torch.empty_like(kb)
+    ids = torch.arange(base, base + c.num_blocks, dtype=torch.int64, device=dev)
+    kb.view(torch.uint8).index_copy_(0, ids, ks.view(torch.uint8))
+    vb.view(torch.uint8).index_copy_(0, ids, vs.view(torch.uint8))
+    del k16, v16
+    small = run_all(pkv, dev, c, dq, ks, vs, c.block_tables, c.num_blocks, fp8)
+    big = run_all(pkv, dev, c, dq, kb, vb, shift_ids(c.block_tables, base), nbig, fp8)
+    names = ["decode", "prefill", "fused decode", "fused prefill"]
+    for name, a, b in zip(names, small[:4], big[:4]):
+        assert a.tobytes() == b.tobytes(), f"{name} differs between the small and the large pool"
+    # The cache write put the same rows in the same logical places.
+    assert torch.equal(small[4], big[4]), "K rows differ"
+    assert torch.equal(small[5], big[5]), "V rows differ"
+    del kb, vb
+    torch.cuda.empty_cache()
+    # Oracle check of the large-pool outputs.
+    rk, rv = oracle.cache_write(c.key_pool, c.value_pool, c.key_new, c.value_new,
+                                oracle.slot_mapping(c.block_tables, c.new_cu_lens, c.new_start_pos, 16))
+    kv_dtype = "bf16"
+    if fp8:
+        rk = ofp8.dequantize(ofp8.quantize_bf16_bits(rk, 0.0123), 0.0123)
+        rv = ofp8.dequantize(ofp8.quantize_bf16_bits(rv, 2.0 ** -5), 2.0 ** -5)
+        kv_dtype = "f64"
+    ctx = (c.chunk_offsets + np.diff(c.cu_q_lens)).astype(np.int32)
+    close(big[0], oracle.decode(dq_host, rk, rv, c.block_tables, ctx, c.scale, "bf16", kv_dtype=kv_dtype),
+          "decode vs oracle")
+    close(big[1], oracle.prefill_chunk(c.query, c.cu_q_lens, c.chunk_offsets, rk, rv, c.block_tables, c.scale,
+                                       "bf16", kv_dtype=kv_dtype), "prefill vs oracle")
