@@ -404,7 +404,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* query, const 
   if (dtype == PKV_DTYPE_BF16 || kv8) {
     DecArgs a{static_cast<const uint16_t*>(query), key_pool, value_pool, block_tables, context_lens, ws_o, ws_ml, out,
               err_flag, max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, max_splits, ob,
-              scale_log2, kv8 ? v_scale : 1.f};
+              scale_log2, kv8 ? v_scale : 1.f, num_seqs};
     // Two resident workgroups per CU at head_dim <= 128 (register bound), one at 256; never more
     // workgroups than the largest possible number of items.
     const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * max_splits;

@@ -4,6 +4,7 @@
 
 #include <cstdlib>
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -96,6 +97,7 @@ struct DecArgs {
   int max_blocks, num_q_heads, num_kv_heads, group, num_blocks, split_tokens, max_splits, out_bf16;
   float scale_log2;  // scale * log2(e), times the K scale for FP8 pools
   float v_scale;     // V scale of an FP8 pool, 1 for bf16
+  int num_seqs;
 };
 
 template <int HD, int E>
@@ -112,7 +114,8 @@ struct DecBuf {
 template <int HD>
 struct DecItem {
   int s, g, split, ctx, nsplit;
-  int my_id[2];  // block ids of the split: lane j holds blocks j and 64 + j
+  int my_id[2];   // block ids of the split: lane j holds blocks j and 64 + j
+  int ref_id[2];  // the neighbouring sequence's ids at the same logical blocks (-2: none)
   bf16x8 qf[DecCfg<HD>::KK];
 };
 
@@ -129,6 +132,17 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   it.my_id[0] = lane < nblk_split ? load_block_id<CHECK>(table, j0 + lane, A_.num_blocks, A_.err_flag) : -1;
   it.my_id[1] = lane + kWave < nblk_split ? load_block_id<CHECK>(table, j0 + kWave + lane, A_.num_blocks, A_.err_flag)
                                           : -1;
+  // The neighbouring sequence's ids (the previous one, or the second for the first): a block it
+  // has at the same logical index is shared (a cached prefix), and is read with a temporal hint so
+  // that it stays in L2 for the other sequences; a false match only changes the hint.
+  const int ref = it.s > 0 ? it.s - 1 : 1;
+  if (ref < A_.num_seqs) {
+    const int32_t* rt = A_.block_tables + static_cast<int64_t>(ref) * A_.max_blocks;
+    it.ref_id[0] = lane < nblk_split ? rt[j0 + lane] : -2;
+    it.ref_id[1] = lane + kWave < nblk_split ? rt[j0 + kWave + lane] : -2;
+  } else {
+    it.ref_id[0] = it.ref_id[1] = -2;
+  }
   // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.  Columns
   // n >= G repeat head G - 1 (their results are never written), so the loads need no select and
   // nothing waits for them before the first MFMA.
@@ -149,6 +163,7 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   using C = DecCfg<HD, E>;
   const int s = it.s, g = it.g, split = it.split, ctx = it.ctx, nsplit = it.nsplit;
   const int my_id0 = it.my_id[0], my_id1 = it.my_id[1];
+  const int ref_id0 = it.ref_id[0], ref_id1 = it.ref_id[1];
   const bf16x8* qf = it.qf;
   const void* __restrict__ key_pool = A_.key_pool;
   const void* __restrict__ value_pool = A_.value_pool;
@@ -184,21 +199,31 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
     const int lane_b = (2 * u) & (kWave - 1);
     B.b0 = __builtin_amdgcn_readlane(idreg, lane_b);
     B.b1 = (t0 + kBlockSize < ctx) ? __builtin_amdgcn_readlane(idreg, lane_b + 1) : -1;
+    // Private blocks are streamed (non-temporal); a step whose first block is shared is not.
+    auto fill = [&](auto temporal) {
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const int b = pg ? B.b1 : B.b0;
+      for (int pg = 0; pg < 2; ++pg) {
+        const int b = pg ? B.b1 : B.b0;
 #pragma unroll
-      for (int i = 0; i < C::VLD; ++i) {
-        if (b >= 0) {
-          const uint32_t cb = c0 + static_cast<uint32_t>(i * C::RPL) * row_bytes;
-          B.k[pg][i] = ld16_nt(pool_at<NARROW>(key_pool, b, blk_bytes, cb));
-          B.v[pg][i] = ld16_nt(pool_at<NARROW>(value_pool, b, blk_bytes, cb));
-        } else {
-          B.k[pg][i] = uint4{0, 0, 0, 0};
-          B.v[pg][i] = uint4{0, 0, 0, 0};
+        for (int i = 0; i < C::VLD; ++i) {
+          if (b >= 0) {
+            const uint32_t cb = c0 + static_cast<uint32_t>(i * C::RPL) * row_bytes;
+            const char* kp = pool_at<NARROW>(key_pool, b, blk_bytes, cb);
+            const char* vp = pool_at<NARROW>(value_pool, b, blk_bytes, cb);
+            B.k[pg][i] = decltype(temporal)::value ? ld16(kp) : ld16_nt(kp);
+            B.v[pg][i] = decltype(temporal)::value ? ld16(vp) : ld16_nt(vp);
+          } else {
+            B.k[pg][i] = uint4{0, 0, 0, 0};
+            B.v[pg][i] = uint4{0, 0, 0, 0};
+          }
         }
       }
-    }
+    };
+    const int refreg = u < kWave / 2 ? ref_id0 : ref_id1;
+    if (B.b0 >= 0 && __builtin_amdgcn_readlane(refreg, lane_b) == B.b0)
+      fill(std::true_type{});
+    else
+      fill(std::false_type{});
   };
 
   auto compute = [&](int u, const DecBuf<HD, E>& B) {

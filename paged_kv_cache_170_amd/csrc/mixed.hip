@@ -121,7 +121,7 @@ extern "C" pkv_status pkv_paged_attn_mixed(
     ws_ml = max_splits > 1 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
     da = DecArgs{static_cast<const uint16_t*>(dec_query), key_pool, value_pool, dec_block_tables, context_lens, ws_o,
                  ws_ml, dec_out, err_flag, dec_max_blocks, num_q_heads, num_kv_heads, group, num_blocks, S,
-                 max_splits, ob, scale_log2, vs};
+                 max_splits, ob, scale_log2, vs, num_dec_seqs};
     // As many workers as the decode launch has workgroups (two per CU), two per workgroup; the
     // workgroup count is a multiple of 8 so that worker indices keep their XCD.
     const int64_t max_items = static_cast<int64_t>(num_dec_seqs) * num_kv_heads * max_splits;
