@@ -12,7 +12,10 @@
 //     `split_tokens` positions of one (sequence, KV head) and serves all G query heads of that
 //     group from each loaded page.
 //   * a wave step covers 32 positions = two 16-token blocks.  K and V rows are fetched whole
-//     (every wave-wide load covers complete rows of the KV head) and staged in LDS;
+//     (every wave-wide load covers complete rows of the KV head) with non-temporal loads, except
+//     blocks the neighbouring sequence also holds at the same logical index (a shared prefix,
+//     "第2章:推理引擎核心技术" §1.5), which are read normally so that they stay in L2 for the other
+//     sequences; rows are staged in LDS;
 //     S^T = K Q^T uses v_mfma_f32_16x16x32_bf16 with the 16 MFMA columns holding the G query
 //     heads (zero-padded), and V is read back transposed with ds_read_b64_tr_b16 as the A operand
 //     of O^T = V^T P^T.
