@@ -235,3 +235,59 @@ def test_fp8_prefill_matches_oracle(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, c
     mx, mean = close(out.cpu().numpy(), ref, "fp8 prefill")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
     assert int(err.item()) == 0
+
+
+def _compact(codes, tables, lens, seqs):
+    """The blocks the listed sequences read, packed into a small pool, and their tables rewritten
+    to it (so the oracle dequantises only what it needs)."""
+    nb = [-(-int(lens[s]) // 16) for s in seqs]
+    ids = np.unique(np.concatenate([tables[s, :n] for s, n in zip(seqs, nb)]))
+    where = {int(b): i for i, b in enumerate(ids)}
+    t = np.full((len(seqs), max(nb)), wl.UNUSED_BLOCK_ID, np.int32)
+    for r, (s, n) in enumerate(zip(seqs, nb)):
+        t[r, :n] = [where[int(b)] for b in tables[s, :n]]
+    return codes[ids], t
+
+
+def test_fp8_mixed_step_full_size(pkv, dev):
+    """The mixed-step workload at full size over E4M3 pools, in the configuration the benchmark
+    runs (library-chosen split size, one workspace): the whole pools quantised by the library's
+    write and compared byte for byte, then the decode of all 127 sequences and the 512-row chunk;
+    sampled sequences and rows against the oracle over the dequantised pools."""
+    _say("case fp8 mixed step: 127 decode sequences + 512-row chunk at 16,384, 64/8 x 128, E4M3 pools")
+    dec, pre = wl.mixed_step(poison=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    nblk, b, hkv, hd = pre.key_pool.shape
+    kp = torch.empty((nblk, b, hkv, hd), dtype=torch.float8_e4m3fn, device=dev)
+    vp = torch.empty_like(kp)
+    pkv.cache_write_fp8(to_dev(pre.key_pool.reshape(nblk * b, hkv, hd), dev, True),
+                        to_dev(pre.value_pool.reshape(nblk * b, hkv, hd), dev, True), kp, vp,
+                        torch.arange(nblk * b, dtype=torch.int32, device=dev), K_SCALE, V_SCALE, err_flag=err)
+    rk = ofp8.quantize_bf16_bits(pre.key_pool, K_SCALE)
+    rv = ofp8.quantize_bf16_bits(pre.value_pool, V_SCALE)
+    rk, rv = write_new(pkv, pre, dev, kp, vp, rk, rv, err)  # the chunk's tokens; whole pools compared
+    d_out = pkv.paged_attn_decode_fp8(to_dev(dec.query, dev, True), kp, vp, to_dev(dec.block_tables, dev),
+                                      to_dev(dec.context_lens, dev), dec.scale, K_SCALE, V_SCALE, err_flag=err)
+    p_out = pkv.paged_attn_prefill_chunk_fp8(to_dev(pre.query, dev, True), to_dev(pre.cu_q_lens, dev),
+                                             to_dev(pre.chunk_offsets, dev), kp, vp, to_dev(pre.block_tables, dev),
+                                             int(np.diff(pre.cu_q_lens).max()), pre.scale, K_SCALE, V_SCALE,
+                                             causal=True, err_flag=err)
+    d_out, p_out = d_out.cpu().numpy(), p_out.cpu().numpy()
+    assert int(err.item()) == 0
+    assert np.isfinite(d_out).all() and np.isfinite(p_out).all()
+    ctx = dec.context_lens
+    seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 1, 63, 126})
+    kc, t = _compact(rk, dec.block_tables, ctx, seqs)
+    vc, _ = _compact(rv, dec.block_tables, ctx, seqs)
+    ref = oracle.decode(dec.query[seqs], ofp8.dequantize(kc, K_SCALE), ofp8.dequantize(vc, V_SCALE), t, ctx[seqs],
+                        dec.scale, "bf16", kv_dtype="f64")
+    mx, mean = close(d_out[seqs], ref, "fp8 mixed decode (sampled sequences)")
+    _say(f"  decode ({len(seqs)} sequences) max-abs {mx:.2e} mean-abs {mean:.2e}")
+    plen = pre.chunk_offsets + np.diff(pre.cu_q_lens)
+    kc, t = _compact(rk, pre.block_tables, plen, [0])
+    vc, _ = _compact(rv, pre.block_tables, plen, [0])
+    rows = np.unique(np.concatenate([np.arange(0, 512, 13), np.arange(500, 512)]))
+    ref = oracle.prefill_chunk(pre.query, pre.cu_q_lens, pre.chunk_offsets, ofp8.dequantize(kc, K_SCALE),
+                               ofp8.dequantize(vc, V_SCALE), t, pre.scale, "bf16", rows=rows, kv_dtype="f64")
+    mx, mean = close(p_out[rows], ref[rows], "fp8 mixed prefill (sampled rows)")
+    _say(f"  prefill ({len(rows)} rows) max-abs {mx:.2e} mean-abs {mean:.2e}")
