@@ -168,9 +168,8 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   const void* __restrict__ key_pool = A_.key_pool;
   const void* __restrict__ value_pool = A_.value_pool;
   const int num_q_heads = A_.num_q_heads, num_kv_heads = A_.num_kv_heads, group = A_.group;
-  const int num_blocks = A_.num_blocks, split_tokens = A_.split_tokens;
+  const int split_tokens = A_.split_tokens;
   const float scale_log2 = A_.scale_log2;
-  int32_t* err_flag = A_.err_flag;
 
   const int lane = threadIdx.x & (kWave - 1), wave = (threadIdx.x / kWave) & (kDecWaves - 1);
   const int n = lane & 15, c = lane >> 4;
