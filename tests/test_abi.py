@@ -117,6 +117,32 @@ def test_host_validation_rejects_bad_arguments():
     fake = ctypes.c_void_p(16)
     assert pre(fake, 0, fake, fake, fake, fake, fake, fake, 2048, 1, 512, 64, 8, 128, 10, 1, 0.1, 1, null, 0, null,
                null) == 3
+    # Fused mixed launch: arguments are checked before any device work; both parts empty is a no-op.
+    mx = lib.pkv_paged_attn_mixed
+
+    def mixed(num_dec=2, num_pre=0, max_q=0, hq=8, hkv=8, hd=64, dtype=1, ks=1.0, vs=1.0, out_dtype=0, split=0,
+              pools=None, scale=0.1):
+        kp = vp = pools
+        return mx(null, null, null, 8, null, num_dec, null, null, null, null, null, 8, num_pre, max_q, 1, kp, vp, 10,
+                  hq, hkv, hd, scale, dtype, ks, vs, out_dtype, split, null, 0, null, 0, null, null)
+    assert mixed(num_dec=0) == 0                           # nothing to do
+    assert mixed(hd=256) == 2                              # two decode workers per workgroup need hd <= 128
+    assert mixed(dtype=0) == 2                             # fp32 pools are not supported here
+    assert mixed(dtype=2, ks=0.0) == 1                     # FP8 pools need finite positive scales
+    assert mixed(hkv=3) == 1                               # heads not a multiple of the KV heads
+    assert mixed(hq=64, hkv=2) == 2                        # group of 32 > 16
+    assert mixed(split=100) == 1                           # split not a multiple of 128
+    assert mixed(scale=float("nan")) == 1
+    assert mixed(out_dtype=2) == 2
+    assert mixed() == 1                                    # decode part with null pointers
+    assert mixed(num_dec=0, num_pre=1, max_q=4) == 1       # prefill part with null pointers
+    # Block copy: block size, head_dim, dtype, empty, null pointers.
+    cb = lib.pkv_copy_blocks
+    assert cb(null, null, null, null, 4, 10, 8, 64, 8, 1, null, null) == 2
+    assert cb(null, null, null, null, 4, 10, 8, 96, 16, 1, null, null) == 2
+    assert cb(null, null, null, null, 0, 10, 8, 64, 16, 1, null, null) == 0
+    assert cb(null, null, null, null, 4, 10, 8, 64, 16, 1, null, null) == 1
+    assert cb(null, null, null, null, -1, 10, 8, 64, 16, 1, null, null) == 1
     # Slot mapping.
     sm = lib.pkv_slot_mapping
     assert sm(null, null, 4, null, null, 2, 5, 10, 8, null, null) == 2
