@@ -13,6 +13,10 @@ Printed: one JSON line.  `value` is the decode KV-read bandwidth in GB/s over un
 `secondary`; `roofline` describes the kernel that takes the most time per step.  Per-kernel
 times come from HIP events on the launch stream.  `cpu_baseline` times the fp64 oracle on this
 host on the same inputs (decode of every sequence, prefill of a sample of rows).
+
+Other workloads (--workload): gqa_decode and long_decode (decode only), and shared_prefix (64
+sequences behind one 4,096-token cached prompt, decoded by the shared-prefix decode, with the
+plain decode on the same inputs timed beside it).
 """
 from __future__ import annotations
 
@@ -40,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixed_step", choices=["mixed_step", "gqa_decode", "long_decode"])
+    ap.add_argument("--workload", default="mixed_step",
+                    choices=["mixed_step", "gqa_decode", "long_decode", "shared_prefix"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="KV pool storage: bf16, or E4M3 codes with per-pool scales (quantised from the bf16 "
                          "pools at setup; the step's new tokens go through the quantising write)")
@@ -143,6 +148,8 @@ def main():
         dec, pre = wl.mixed_step(poison=False)
     elif args.workload == "gqa_decode":
         dec, pre = wl.gqa_decode(poison=False), None
+    elif args.workload == "shared_prefix":
+        dec, pre = wl.shared_prefix_decode(poison=False), None
     else:
         dec, pre = wl.long_decode(poison=False), None
     gen_s = time.perf_counter() - t_gen
@@ -184,6 +191,14 @@ def main():
     d_bt, d_ctx = to_dev(dec.block_tables), to_dev(dec.context_lens)
     d_out = torch.empty((dec.num_seqs, dec.num_q_heads, dec.head_dim), dtype=torch.float32, device=dev)
     ws = pkv.decode_workspace(d_q, dec.num_kv_heads, dec.max_blocks_per_seq)
+    # Shared-prefix workload: the decode attends the shared blocks once for all members.
+    pfx = args.workload == "shared_prefix"
+    if pfx:
+        if fp8:
+            raise SystemExit("the shared-prefix decode takes bf16 pools")
+        d_members = to_dev(dec.notes["members"])
+        pfx_blocks = int(dec.notes["prefix_blocks"])
+        ws = pkv.decode_prefix_workspace(d_q, dec.num_kv_heads, dec.max_blocks_per_seq)
     if pre is not None:
         p_q = to_dev(pre.query, bf)
         p_cu, p_off, p_bt = to_dev(pre.cu_q_lens), to_dev(pre.chunk_offsets), to_dev(pre.block_tables)
@@ -222,6 +237,9 @@ def main():
         mark(2)
         if fp8:
             pkv.paged_attn_decode_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, out=d_out, workspace=ws)
+        elif pfx:
+            pkv.paged_attn_decode_prefix(d_q, kp, vp, d_bt, d_ctx, dec.scale, d_members, pfx_blocks, out=d_out,
+                                         workspace=ws)
         else:
             pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=d_out, workspace=ws)
         mark(3)
@@ -319,6 +337,28 @@ def main():
         fused_info = {"fused_ms": times["fused"], "separate_ms": times["separate"],
                       "speedup": times["separate"] / times["fused"]}
 
+    # Shared-prefix workload: the plain decode on the same inputs (every shared block read once per
+    # member, mostly from L2), for comparison.
+    plain_info = None
+    if pfx:
+        p_out = torch.empty_like(d_out)
+        pws = pkv.decode_workspace(d_q, dec.num_kv_heads, dec.max_blocks_per_seq)
+        pt = 1e9
+        for _ in range(3):
+            pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=p_out, workspace=pws)
+            e0.record(stream)
+            for _ in range(10):
+                pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=p_out, workspace=pws)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pt = min(pt, e0.elapsed_time(e1) / 10)
+        step()
+        torch.cuda.synchronize()
+        plain_info = {"plain_decode_ms": pt, "prefix_decode_ms": avg_ms["decode"],
+                      "speedup": pt / avg_ms["decode"], "max_abs_diff": float((p_out - d_out).abs().max()),
+                      "members": int(len(dec.notes["members"])), "prefix_blocks": pfx_blocks}
+        del p_out, pws
+
     # Copy-on-write block copies on this pool: 512 disjoint pairs (K and V, read + written).
     nblk = dec.num_blocks
     cp = torch.randperm(nblk, device="cpu")[:1024].to(torch.int32)
@@ -335,10 +375,11 @@ def main():
     copy_info = {"pairs": 512, "ms": copy_ms, "gbs": 4 * 512 * block_bytes / (copy_ms * 1e-3) / 1e9}
 
     # Host-side block manager on the decode batch's shape: every sequence is added (a shared
-    # prefix of 63 full blocks, as in the mixed step), extended by one decode token, and freed.
+    # prefix of full blocks: the workload's own, else 63 as in the mixed step), extended by one
+    # decode token, and freed.
     bm = pkv.BlockManager(nblk)
     rows = np.full((dec.num_seqs, dec.max_blocks_per_seq), -1, np.int32)
-    prefix = np.arange(63 * 16, dtype=np.int32)
+    prefix = np.arange(int((dec.notes or {}).get("prefix_blocks", 63)) * 16, dtype=np.int32)
     prompts = [np.concatenate([prefix, np.full(max(int(c) - 1 - prefix.size, 0), 100000 + s, np.int32)])[: int(c) - 1]
                for s, c in enumerate(dec.context_lens)]
     t_bm = time.perf_counter()
@@ -365,6 +406,7 @@ def main():
         "stream_read_gbs": stream_gbs,
         "decode_frac_of_stream_read": dec_gbs / stream_gbs,
         "fused_mixed_step": fused_info,
+        "shared_prefix_vs_plain": plain_info,
         "copy_blocks": copy_info,
         "block_manager_host": bm_info,
     }
@@ -407,9 +449,12 @@ def main():
 
     config = {"workload": args.workload, "num_seqs_decode": dec.num_seqs, "q_heads": dec.num_q_heads,
               "kv_heads": dec.num_kv_heads, "head_dim": dec.head_dim, "block_size": 16,
-              "context_lens": "uniform 200..8192, shared 63-block prefix" if args.workload == "mixed_step" else
-              ("lognormal mean 1500, sd 600, clipped 16..8192" if args.workload == "gqa_decode" else "4096 each"),
-              "seed": {"mixed_step": 5, "gqa_decode": 3, "long_decode": 4}[args.workload],
+              "context_lens": {"mixed_step": "uniform 200..8192, shared 63-block prefix",
+                               "gqa_decode": "lognormal mean 1500, sd 600, clipped 16..8192",
+                               "long_decode": "4096 each",
+                               "shared_prefix": "shared 256-block (4,096-token) prefix + uniform 1..512 private"
+                               }[args.workload],
+              "seed": {"mixed_step": 5, "gqa_decode": 3, "long_decode": 4, "shared_prefix": 6}[args.workload],
               "kv_storage": "fp8_e4m3 (k_scale = v_scale = 2^-5)" if fp8 else ("bf16" if bf else "f32")}
     if pre is not None:
         config.update({"prefill_chunk": int(pre.cu_q_lens[-1]), "prefill_offset": int(pre.chunk_offsets[0])})

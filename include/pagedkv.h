@@ -234,6 +234,40 @@ pkv_status pkv_cache_write_fp8(const void* key, const void* value, int64_t key_t
                                pkv_dtype in_dtype, float k_scale, float v_scale, int32_t* err_flag, void* stream);
 
 /*
+ * Decode with a shared prefix ([Engine-core] §1.5 and §3.2: sequences that share a cached prefix
+ * map its logical blocks to the same physical blocks).  Computes exactly what
+ * pkv_paged_attn_decode computes (up to rounding order), attending the shared prefix once per KV
+ * head for all member sequences together instead of once per sequence.
+ *   prefix_members  device int32 [num_members]: distinct sequence indices whose block-table rows
+ *                   all start with the same prefix_blocks physical ids (those of
+ *                   prefix_members[0]) and whose context_lens are at least prefix_blocks * 16;
+ *                   the caller guarantees this (a row that differs gives a wrong result for that
+ *                   sequence; an index outside [0, num_seqs) sets PKV_FLAG_BAD_LENGTH in checked
+ *                   mode and is skipped, and if it is prefix_members[0] the members' outputs are
+ *                   undefined; a member shorter than the prefix sets the same flag)
+ *   prefix_blocks   number of shared leading blocks (0 <= prefix_blocks <= max_blocks_per_seq)
+ *   workspace       at least pkv_decode_prefix_workspace_bytes(...) bytes (16-byte aligned)
+ * Other arguments as for pkv_paged_attn_decode; BF16 pools, head_dim 64 or 128.  With no members
+ * or prefix_blocks == 0 this is pkv_paged_attn_decode with the same split size.
+ * Work: the (member, query head) pairs of a KV head are the rows of an MFMA attention over the
+ * prefix (one partial per key split), run in the same launch as the decode of every position past
+ * the prefix; the split reduce merges the two.  It pays when the prefix is long against the
+ * members' own positions; the plain decode reads a short shared prefix from L2 almost for free.
+ */
+pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                        const void* value_pool, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t num_blocks, float scale, pkv_dtype dtype,
+                                        const int32_t* prefix_members, int32_t num_members, int32_t prefix_blocks,
+                                        int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                        int32_t* err_flag, void* stream);
+
+/* Workspace bytes of pkv_paged_attn_decode_prefix for these shapes (0 for unsupported shapes). */
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_blocks_per_seq, int32_t split_tokens);
+
+/*
  * Decode over FP8 pools ([Chunked-Prefill] section on prefill and decode; [Engine-core] §1.4):
  * pkv_paged_attn_decode with K_s[j] and V_s[j] replaced by their dequantised
  * values value(code) * k_scale and value(code) * v_scale.  query is bf16; out F32 or BF16.  The

@@ -42,6 +42,9 @@ _SIGS = {
                                 _vp, _vp]),
     "pkv_decode_split_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_decode_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_paged_attn_decode_prefix": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                            _f32, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                      _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -432,6 +435,46 @@ def paged_attn_decode(query: torch.Tensor, key_pool: torch.Tensor, value_pool: t
                                       nblk, float(scale), _dtype_code(key_pool), int(split_tokens),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _ptr(err_flag), _stream(query.device)), "pkv_paged_attn_decode")
+    return out
+
+
+def decode_prefix_workspace(query: torch.Tensor, num_kv_heads: int, max_blocks_per_seq: int,
+                            split_tokens: int = 0) -> torch.Tensor:
+    """Allocate a workspace for pkv_paged_attn_decode_prefix (a byte tensor on the query's device)."""
+    n = int(_lib.pkv_decode_prefix_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads, query.shape[2],
+                                                   max_blocks_per_seq, split_tokens))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=query.device)
+
+
+def paged_attn_decode_prefix(query: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                             prefix_members: torch.Tensor, prefix_blocks: int, out: torch.Tensor | None = None,
+                             out_dtype: torch.dtype = torch.float32, workspace: torch.Tensor | None = None,
+                             split_tokens: int = 0, err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode with a shared prefix attended once per KV head; see pkv_paged_attn_decode_prefix."""
+    _need_gpu(query, key_pool, value_pool, block_tables, context_lens, prefix_members, out, workspace, err_flag)
+    _need_i32(block_tables, context_lens, prefix_members, err_flag)
+    if prefix_members.dim() != 1 or not prefix_members.is_contiguous():
+        raise ValueError("prefix_members must be a contiguous 1-D int32 tensor")
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != key_pool.dtype or not query.is_contiguous():
+        raise ValueError("query must be contiguous [num_seqs, num_q_heads, head_dim] in the pool dtype")
+    B, hq, _ = query.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((B, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (B, hq, hd):
+        raise ValueError("out must be contiguous [num_seqs, num_q_heads, head_dim]")
+    if workspace is None:
+        workspace = decode_prefix_workspace(query, hkv, block_tables.shape[1], split_tokens)
+    _check(_lib.pkv_paged_attn_decode_prefix(_ptr(out), _dtype_code(out), _ptr(query), _ptr(key_pool),
+                                             _ptr(value_pool), _ptr(block_tables), block_tables.shape[1],
+                                             _ptr(context_lens), B, hq, hkv, hd, nblk, float(scale),
+                                             _dtype_code(key_pool), _ptr(prefix_members), prefix_members.shape[0],
+                                             int(prefix_blocks), int(split_tokens), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _ptr(err_flag),
+                                             _stream(query.device)), "pkv_paged_attn_decode_prefix")
     return out
 
 

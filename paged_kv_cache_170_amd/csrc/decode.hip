@@ -24,27 +24,58 @@
 //     no cross-lane max); the 4 waves' states merge in LDS, and a split's (o, m, l) goes to the workspace unless the sequence
 //     fits one split, in which case the normalised row is written directly.
 //   * fp32 pools take a plain VALU kernel with the same split/merge structure.
+//   * pkv_paged_attn_decode_prefix: the members of a shared prefix (§1.5) get the prefix attended
+//     once per KV head by MFMA prefix items placed in front of the decode workers of the same
+//     launch (mixed.hip); the reduce merges those partials with the members' own splits.
 #include "decode_dev.hpp"
+#include "prefill_dev.hpp"
 
 namespace pkv {
 
+// Shared-prefix decode (members != null): the plan first marks the member sequences in
+// member_out; a member's pieces then cover its positions after the prefix_blocks shared blocks
+// (a member whose context ends with the prefix gets no piece: the prefix partial is its result).
 template <bool CHECK>
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t* __restrict__ context_lens,
                                                                    int num_seqs, int max_blocks, int split_tokens,
                                                                    int2* __restrict__ pieces,
                                                                    int32_t* __restrict__ plan, int grid, int queues,
-                                                                   int32_t* err_flag) {
+                                                                   int32_t* err_flag, const int32_t* __restrict__ members,
+                                                                   int num_members, int prefix_blocks,
+                                                                   uint8_t* __restrict__ member_out) {
   __shared__ int count[kMaxClasses];
   __shared__ int cursor[kMaxClasses];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int top = split_tokens / 32;  // class of a full split (<= 64)
   if (tid < kMaxClasses) count[tid] = 0;
+  if (members != nullptr) {
+    for (int s = tid; s < num_seqs; s += kPlanThreads) member_out[s] = 0;
+    __syncthreads();
+    for (int i = tid; i < num_members; i += kPlanThreads) {
+      const int m = members[i];
+      if (m >= 0 && m < num_seqs) member_out[m] = 1;
+    }
+  }
   __syncthreads();
+  // Context of the pieces: the whole context, or a member's positions past the prefix.
+  auto piece_ctx = [&](int s, bool report, bool& member) {
+    int ctx = clamp_ctx<CHECK>(context_lens[s], max_blocks, err_flag, report);
+    member = members != nullptr && member_out[s];
+    if (member) {
+      ctx -= prefix_blocks * kBlockSize;
+      if (ctx < 0) {
+        if (CHECK && report) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+        ctx = 0;
+      }
+    }
+    return ctx;
+  };
   for (int s = tid; s < num_seqs; s += kPlanThreads) {
-    const int ctx = clamp_ctx<CHECK>(context_lens[s], max_blocks, err_flag, true);
+    bool member;
+    const int ctx = piece_ctx(s, true, member);
     const int full = ctx / split_tokens, rem = ctx - full * split_tokens;
     if (full) atomicAdd(&count[top], full);
-    if (rem || !ctx) atomicAdd(&count[rem ? (rem + 31) / 32 : 1], 1);
+    if (rem || (!ctx && !member)) atomicAdd(&count[rem ? (rem + 31) / 32 : 1], 1);
   }
   __syncthreads();
   if (tid < kWave) {
@@ -63,14 +94,15 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
   if (tid < queues) plan[tid * kCounterStride] = 2 * (grid / queues);
   __syncthreads();
   for (int s = tid; s < num_seqs; s += kPlanThreads) {
-    const int ctx = clamp_ctx<false>(context_lens[s], max_blocks, nullptr, false);
+    bool member;
+    const int ctx = piece_ctx(s, false, member);
     const int full = ctx / split_tokens, rem = ctx - full * split_tokens;
     const int tag = static_cast<int>(static_cast<uint32_t>(s) << 16);
     if (full) {
       const int at = atomicAdd(&cursor[top], full);
       for (int k = 0; k < full; ++k) pieces[at + k] = int2{tag | k, ctx};
     }
-    if (rem || !ctx) pieces[atomicAdd(&cursor[rem ? (rem + 31) / 32 : 1], 1)] = int2{tag | full, ctx};
+    if (rem || (!ctx && !member)) pieces[atomicAdd(&cursor[rem ? (rem + 31) / 32 : 1], 1)] = int2{tag | full, ctx};
   }
 }
 
@@ -208,39 +240,46 @@ __global__ __launch_bounds__(kDecThreads) void decode_f32_kernel(
     }
   }
   __syncthreads();
-  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, max_splits, num_q_heads, ws_o, ws_ml, out, out_bf16,
-                  1.f);
+  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit == 1, max_splits, num_q_heads, ws_o, ws_ml, out,
+                  out_bf16, 1.f);
 }
 
 // Log-sum-exp merge of split partials: grid (num_kv_heads, num_seqs); the 256 threads cover the
 // group's query heads x head_dim.  Sequences that fit one split were finished by the main kernel.
+// Shared-prefix decode (member != null): a member's parts are its splits past the prefix (slots
+// 0 .. nsplit - 1) and the prefix_parts prefix partials (slots prefix_slot0 ..), always merged.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_ml,
                                                             const int32_t* __restrict__ context_lens, int max_blocks,
                                                             int num_q_heads, int group, int head_dim,
-                                                            int split_tokens, int max_splits, void* __restrict__ out,
-                                                            int out_bf16) {
+                                                            int split_tokens, int slots, void* __restrict__ out,
+                                                            int out_bf16, const uint8_t* __restrict__ member,
+                                                            int prefix_blocks, int prefix_slot0, int prefix_parts) {
   const int g = blockIdx.x, s = blockIdx.y;
   int ctx = context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > max_blocks * kBlockSize ? max_blocks * kBlockSize : ctx);
+  const bool is_member = member != nullptr && member[s];
+  if (is_member) ctx = max(ctx - prefix_blocks * kBlockSize, 0);
   const int nsplit = (ctx + split_tokens - 1) / split_tokens;
-  if (nsplit <= 1) return;
+  if (!is_member && nsplit <= 1) return;
+  const int nparts = nsplit + (is_member ? prefix_parts : 0);
   // Each thread owns four consecutive head_dim elements of one query head (16-byte loads).
   const int quads = head_dim / 4;
   for (int i = threadIdx.x; i < group * quads; i += blockDim.x) {
     const int hn = i / quads, d = 4 * (i - hn * quads);
     const int h = g * group + hn;
-    const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_splits;
-    // One pass with a running max; the loads of a batch of splits are independent and issue together.
+    const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * slots;
+    // One pass with a running max; the loads of a batch of parts are independent and issue together.
     float M = -INFINITY, L = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p0 = 0; p0 < nsplit; p0 += 8) {
+    for (int p0 = 0; p0 < nparts; p0 += 8) {
       float2 ml[8];
       float4 op[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const bool live = p0 + k < nsplit;
-        const int64_t part = base + (live ? p0 + k : p0);
+        const bool live = p0 + k < nparts;
+        const int pk = live ? p0 + k : p0;
+        const int64_t part = base + (pk < nsplit ? pk : prefix_slot0 + pk - nsplit);
         ml[k] = *reinterpret_cast<const float2*>(ws_ml + part * 2);
         if (!live) ml[k].x = -INFINITY;
         op[k] = *reinterpret_cast<const float4*>(ws_o + part * head_dim + d);
@@ -288,21 +327,25 @@ using namespace pkv;
 using namespace pkv_dec;
 
 void pkv_dec::launch_plan(bool check, const int32_t* context_lens, int num_seqs, int max_blocks, int split_tokens,
-                          int2* pieces, int32_t* plan, int grid, int queues, int32_t* err_flag, hipStream_t st) {
+                          int2* pieces, int32_t* plan, int grid, int queues, int32_t* err_flag, hipStream_t st,
+                          const int32_t* members, int num_members, int prefix_blocks, uint8_t* member_out) {
   if (check)
     hipLaunchKernelGGL((decode_plan_kernel<true>), dim3(1), dim3(kPlanThreads), 0, st, context_lens, num_seqs,
-                       max_blocks, split_tokens, pieces, plan, grid, queues, err_flag);
+                       max_blocks, split_tokens, pieces, plan, grid, queues, err_flag, members, num_members,
+                       prefix_blocks, member_out);
   else
     hipLaunchKernelGGL((decode_plan_kernel<false>), dim3(1), dim3(kPlanThreads), 0, st, context_lens, num_seqs,
-                       max_blocks, split_tokens, pieces, plan, grid, queues, err_flag);
+                       max_blocks, split_tokens, pieces, plan, grid, queues, err_flag, members, num_members,
+                       prefix_blocks, member_out);
 }
 
 void pkv_dec::launch_reduce(const float* ws_o, const float* ws_ml, const int32_t* context_lens, int max_blocks,
                             int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int split_tokens,
-                            int max_splits, void* out, int out_bf16, hipStream_t st) {
+                            int slots, void* out, int out_bf16, hipStream_t st, const uint8_t* member,
+                            int prefix_blocks, int prefix_slot0, int prefix_parts) {
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(num_kv_heads, num_seqs), dim3(256), 0, st, ws_o, ws_ml, context_lens,
-                     max_blocks, num_q_heads, num_q_heads / num_kv_heads, head_dim, split_tokens, max_splits, out,
-                     out_bf16);
+                     max_blocks, num_q_heads, num_q_heads / num_kv_heads, head_dim, split_tokens, slots, out,
+                     out_bf16, member, prefix_blocks, prefix_slot0, prefix_parts);
 }
 
 namespace {
@@ -407,7 +450,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* query, const 
   if (dtype == PKV_DTYPE_BF16 || kv8) {
     DecArgs a{static_cast<const uint16_t*>(query), key_pool, value_pool, block_tables, context_lens, ws_o, ws_ml, out,
               err_flag, max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, max_splits, ob,
-              scale_log2, kv8 ? v_scale : 1.f, num_seqs};
+              scale_log2, kv8 ? v_scale : 1.f, num_seqs, nullptr, 0, max_splits};
     // Two resident workgroups per CU at head_dim <= 128 (register bound), one at 256; never more
     // workgroups than the largest possible number of items.
     const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * max_splits;
@@ -478,4 +521,148 @@ extern "C" pkv_status pkv_paged_attn_decode_fp8(void* out, pkv_dtype out_dtype, 
   return decode_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale, PKV_DTYPE_FP8_E4M3, k_scale,
                      v_scale, split_tokens, workspace, workspace_bytes, err_flag, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Shared-prefix decode.  Member sequences share their first prefix_blocks physical blocks (a
+// cached prefix, [Engine-core] §1.5 / §3.2).  The prefix is attended once per KV head for all
+// members together: the prefill kernel in shared-prefix mode takes the (member, query head) pairs
+// as its rows and writes one (o, m, l) partial per key split; the decode then covers each member's
+// positions past the prefix, and the reduce merges both (log-sum-exp combine, the same identity
+// as the split reduce).  Non-members are decoded as by pkv_paged_attn_decode.
+
+namespace {
+
+struct PfxLayout {
+  WsLayout base;
+  size_t member, total;
+  int slots, max_splits;
+};
+
+PfxLayout pfx_layout(int32_t num_seqs, int32_t hq, int32_t hd, int32_t max_blocks, int32_t S) {
+  PfxLayout l;
+  l.max_splits = static_cast<int>((static_cast<int64_t>(max_blocks) * kBlockSize + S - 1) / S);
+  l.slots = l.max_splits + kPreMaxSplit;
+  l.base = ws_layout(num_seqs, hq, hd, l.slots);
+  l.member = round256(l.base.total);
+  l.total = l.member + round256(static_cast<size_t>(num_seqs));
+  return l;
+}
+
+}  // namespace
+
+extern "C" size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                                    int32_t split_tokens) {
+  if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return 0;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 2048) return 0;
+  const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+  return pfx_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, S).total;
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtype, const void* query,
+                                                   const void* key_pool, const void* value_pool,
+                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                   const int32_t* context_lens, int32_t num_seqs,
+                                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t num_blocks, float scale, pkv_dtype dtype,
+                                                   const int32_t* prefix_members, int32_t num_members,
+                                                   int32_t prefix_blocks, int32_t split_tokens, void* workspace,
+                                                   size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_members < 0 || prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq || num_members > num_seqs)
+    return PKV_ERR_INVALID_ARG;
+  if (split_tokens < 0 || split_tokens % 128 != 0 || split_tokens > 2048) return PKV_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!shapes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq)) return PKV_ERR_UNSUPPORTED;
+  if (head_dim > 128) return PKV_ERR_UNSUPPORTED;  // the prefix pass uses the prefill kernel's key splits
+  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!out || !query || !key_pool || !value_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (num_members > 0 && prefix_blocks > 0 && !prefix_members) return PKV_ERR_INVALID_ARG;
+  for (const void* p : {static_cast<const void*>(out), query, key_pool, value_pool, static_cast<const void*>(workspace)})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARG;
+  const int32_t S = resolve_split(split_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+  const PfxLayout lay = pfx_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, S);
+  if (!workspace || workspace_bytes < lay.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  // No shared prefix: the ordinary decode (its layout fits in this one).
+  if (num_members == 0 || prefix_blocks == 0)
+    return pkv_paged_attn_decode(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq,
+                                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale,
+                                 dtype, S, workspace, workspace_bytes, err_flag, stream);
+  if (static_cast<int64_t>(num_seqs) * lay.max_splits * num_kv_heads > INT32_MAX / 2) return PKV_ERR_UNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* plan = reinterpret_cast<int32_t*>(ws);
+  int2* pieces = reinterpret_cast<int2*>(ws + lay.base.pieces);
+  float* ws_o = reinterpret_cast<float*>(ws + lay.base.o);
+  float* ws_ml = reinterpret_cast<float*>(ws + lay.base.ml);
+  uint8_t* member = reinterpret_cast<uint8_t*>(ws + lay.member);
+  const int group = num_q_heads / num_kv_heads;
+  const float scale_log2 = scale * kLog2e;
+  const int ob = out_dtype == PKV_DTYPE_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool check = err_flag != nullptr;
+  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
+                      num_blocks < (1 << 24);
+
+  // Prefix pass: rows (member, query head) of each KV head, key splits of the prefix.
+  const int q_tiles = static_cast<int>((static_cast<int64_t>(num_members) * group + kPreTile - 1) / kPreTile);
+  const int64_t row_items = static_cast<int64_t>(q_tiles) * num_kv_heads;
+  // Key splits of the prefix: enough items to fill the chip, but each split adds a partial per
+  // (member, query head) that is written and read back (M*G*hd*8 bytes per KV head against the
+  // prefix's 64*P*hd); halve the splits while that traffic exceeds four times the prefix's.
+  int kp = pkv_pre::ksplit_for(row_items, prefix_blocks, head_dim, pkv_host::cu_count());
+  while (kp > 1 && static_cast<int64_t>(kp) * num_members * group > 32 * static_cast<int64_t>(prefix_blocks)) kp /= 2;
+  PreArgs pa{};
+  pa.query = static_cast<const uint16_t*>(query);
+  pa.key_pool = key_pool;
+  pa.value_pool = value_pool;
+  pa.block_tables = block_tables;
+  pa.max_blocks = max_blocks_per_seq;
+  pa.q_tiles = q_tiles;
+  pa.num_q_heads = num_q_heads;
+  pa.num_kv_heads = num_kv_heads;
+  pa.group = group;
+  pa.num_blocks = num_blocks;
+  pa.causal = 0;
+  pa.scale_log2 = scale_log2;
+  pa.v_scale = 1.f;
+  pa.err_flag = err_flag;
+  pa.ksplit = kp;
+  pa.ws_o = ws_o;
+  pa.ws_ml = ws_ml;
+  pa.prefix_members = prefix_members;
+  pa.num_members = num_members;
+  pa.prefix_blocks = prefix_blocks;
+  pa.prefix_slots = lay.slots;
+  pa.prefix_slot0 = lay.max_splits;
+  pa.prefix_num_seqs = num_seqs;
+  // Plan: members marked, their pieces past the prefix; as many decode workers as the decode
+  // launch has workgroups (two per CU), two per 512-thread workgroup, the workgroup count a
+  // multiple of 8 so that worker indices keep their XCD.
+  const int64_t max_items = static_cast<int64_t>(num_seqs) * num_kv_heads * lay.max_splits;
+  const int64_t want = 2 * static_cast<int64_t>(pkv_host::cu_count());
+  const int64_t workers = max_items < want ? max_items : want;
+  const int dec_wgs = static_cast<int>((workers + 15) / 16 * 8);
+  const int nworkers = 2 * dec_wgs;
+  const int queues = nworkers % kMaxQueues == 0 ? kMaxQueues : 8;
+  launch_plan(check, context_lens, num_seqs, max_blocks_per_seq, S, pieces, plan, nworkers, queues, err_flag, st,
+              prefix_members, num_members, prefix_blocks, member);
+  if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+
+  // One launch: the prefix items, then the decode of everything else (every member item leaves a
+  // partial), then the reduce merges both.
+  const DecArgs a{static_cast<const uint16_t*>(query), key_pool, value_pool, block_tables, context_lens, ws_o, ws_ml,
+                  out, err_flag, max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, lay.max_splits,
+                  ob, scale_log2, 1.f, num_seqs, member, prefix_blocks, lay.slots};
+  const int64_t pre_items = row_items * kp;
+  if (pre_items + dec_wgs + 8 > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  launch_prefix_decode(a, pieces, plan, queues, dec_wgs, pa, static_cast<int>(pre_items), head_dim, check, narrow, st);
+  if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+  launch_reduce(ws_o, ws_ml, context_lens, max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, S,
+                lay.slots, out, ob, st, member, prefix_blocks, lay.max_splits, kp);
+  return pkv_host::launch_status();
 }

@@ -39,9 +39,11 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool 
 }
 
 // Merges the per-wave states held in LDS and writes either the final rows or the split partial.
+// slots: partial slots per (sequence, query head) row of the workspace; final: the item is the
+// sequence's only part (one split and no shared-prefix partial), so it writes the normalised row.
 template <int HD>
 __device__ __forceinline__ void merge_waves(const float* comb_o, const float* comb_ml, int group, int s, int g,
-                                            int split, int nsplit, int max_splits, int num_q_heads, float* ws_o,
+                                            int split, bool final, int slots, int num_q_heads, float* ws_o,
                                             float* ws_ml, void* out, bool out_bf16, float v_scale) {
   for (int i = threadIdx.x & (kDecThreads - 1); i < group * HD; i += kDecThreads) {
     const int hn = i / HD, d = i - hn * HD;
@@ -60,10 +62,10 @@ __device__ __forceinline__ void merge_waves(const float* comb_o, const float* co
     const int64_t row = static_cast<int64_t>(s) * num_q_heads + h;
     // v_scale: the FP8 pool's V scale (1 for bf16 pools, where the product is exact).
     O *= v_scale;
-    if (nsplit == 1) {
+    if (final) {
       store_out(out, row * HD + d, L > 0.f ? O / L : 0.f, out_bf16);
     } else {
-      const int64_t part = row * max_splits + split;
+      const int64_t part = row * slots + split;
       ws_o[part * HD + d] = O;
       if (d == 0) {
         ws_ml[part * 2] = M;
@@ -84,6 +86,8 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int32_t* err_f
 }
 
 // Kernel arguments of the bf16 decode (one struct so that every launch form shares them).
+struct PreArgs;  // prefill_dev.hpp
+
 struct DecArgs {
   const uint16_t* query;
   const void* key_pool;    // bf16 or E4M3 codes
@@ -98,6 +102,12 @@ struct DecArgs {
   float scale_log2;  // scale * log2(e), times the K scale for FP8 pools
   float v_scale;     // V scale of an FP8 pool, 1 for bf16
   int num_seqs;
+  // Shared-prefix decode (member != null): member[s] marks the sequences whose first
+  // prefix_blocks blocks are the shared prefix; their items cover the positions after it (their
+  // table rows and contexts are read past it) and always write partials, which the reduce merges
+  // with the prefix partials.  slots: partial slots per (sequence, query head) row.
+  const uint8_t* member;
+  int prefix_blocks, slots;
 };
 
 template <int HD, int E>
@@ -114,6 +124,7 @@ struct DecBuf {
 template <int HD>
 struct DecItem {
   int s, g, split, ctx, nsplit;
+  int tbl0;  // first logical block of the item's table view (the prefix length for members, else 0)
   int my_id[2];   // block ids of the split: lane j holds blocks j and 64 + j
   int ref_id[2];  // the neighbouring sequence's ids at the same logical blocks (-2: none)
   bf16x8 qf[DecCfg<HD>::KK];
@@ -125,7 +136,7 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   const int n = lane & 15, c = lane >> 4;
   const int tok0 = it.split * A_.split_tokens;
   const int tok_end = min(tok0 + A_.split_tokens, it.ctx);
-  const int32_t* table = A_.block_tables + static_cast<int64_t>(it.s) * A_.max_blocks;
+  const int32_t* table = A_.block_tables + static_cast<int64_t>(it.s) * A_.max_blocks + it.tbl0;
   // The split's block ids, two per lane (a split spans at most 128 blocks).
   const int nblk_split = it.ctx > 0 ? (tok_end - tok0 + kBlockSize - 1) / kBlockSize : 0;
   const int j0 = tok0 / kBlockSize;
@@ -137,7 +148,7 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   // that it stays in L2 for the other sequences; a false match only changes the hint.
   const int ref = it.s > 0 ? it.s - 1 : 1;
   if (ref < A_.num_seqs) {
-    const int32_t* rt = A_.block_tables + static_cast<int64_t>(ref) * A_.max_blocks;
+    const int32_t* rt = A_.block_tables + static_cast<int64_t>(ref) * A_.max_blocks + it.tbl0;
     it.ref_id[0] = lane < nblk_split ? rt[j0 + lane] : -2;
     it.ref_id[1] = lane + kWave < nblk_split ? rt[j0 + kWave + lane] : -2;
   } else {
@@ -343,7 +354,9 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
     comb_ml[(wave * kMaxGroup + n) * 2 + 1] = l_run;
   }
   sync();
-  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, nsplit, A_.max_splits, num_q_heads, A_.ws_o, A_.ws_ml, A_.out,
+  // A shared-prefix member always leaves a partial: the reduce merges it with the prefix's.
+  const bool final = nsplit == 1 && it.tbl0 == 0;
+  merge_waves<HD>(comb_o, comb_ml, group, s, g, split, final, A_.slots, num_q_heads, A_.ws_o, A_.ws_ml, A_.out,
                   A_.out_bf16, A_.v_scale);
 }
 
@@ -388,6 +401,7 @@ __device__ __forceinline__ void decode_worker(const DecArgs& a, const int2* __re
     it.g = item - piece * a.num_kv_heads;
     it.ctx = code.y;
     it.nsplit = (it.ctx + a.split_tokens - 1) / a.split_tokens;
+    it.tbl0 = (a.member != nullptr && a.member[it.s]) ? a.prefix_blocks : 0;
   };
   int cur_i = worker, nxt_i = worker + nworkers;
   if (cur_i >= total) return;  // uniform over the worker's threads
@@ -454,11 +468,24 @@ inline WsLayout ws_layout(int32_t num_seqs, int32_t hq, int32_t hd, int64_t max_
 }
 
 // Launch the one-workgroup plan pass (decode.hip).
+// members / num_members / prefix_blocks / member_out: the shared-prefix decode (null / 0 otherwise).
 void launch_plan(bool check, const int32_t* context_lens, int num_seqs, int max_blocks, int split_tokens,
-                 int2* pieces, int32_t* plan, int grid, int queues, int32_t* err_flag, hipStream_t st);
+                 int2* pieces, int32_t* plan, int grid, int queues, int32_t* err_flag, hipStream_t st,
+                 const int32_t* members = nullptr, int num_members = 0, int prefix_blocks = 0,
+                 uint8_t* member_out = nullptr);
+// Launch the shared-prefix decode (mixed.hip): the prefix items (prefill kernel in shared-prefix
+// mode, pre_items workgroups) first, then dec_wgs workgroups of two decode workers each, in one
+// launch; head_dim 64 or 128, bf16 pools.
+void launch_prefix_decode(const pkv::DecArgs& da, const int2* pieces, int32_t* plan, int queues, int dec_wgs,
+                          const pkv::PreArgs& pa, int pre_items, int32_t head_dim, bool check, bool narrow,
+                          hipStream_t st);
 // Launch the split reduce (decode.hip).
+// slots: partial slots per (sequence, query head); member / prefix_blocks / prefix_slot0 /
+// prefix_parts: the shared-prefix decode, whose members also merge prefix_parts partials from slot
+// prefix_slot0 on (null / 0 otherwise).
 void launch_reduce(const float* ws_o, const float* ws_ml, const int32_t* context_lens, int max_blocks,
-                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int split_tokens, int max_splits,
-                   void* out, int out_bf16, hipStream_t st);
+                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int split_tokens, int slots,
+                   void* out, int out_bf16, hipStream_t st, const uint8_t* member = nullptr, int prefix_blocks = 0,
+                   int prefix_slot0 = 0, int prefix_parts = 0);
 
 }  // namespace pkv_dec

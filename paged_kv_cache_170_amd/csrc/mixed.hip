@@ -29,10 +29,14 @@ struct MixCfg {
 template <int HD, bool CHECK, bool NARROW, bool KV8>
 __global__ __launch_bounds__(kPreThreads) void mixed_step_kernel(DecArgs da, const int2* __restrict__ pieces,
                                                                  int32_t* __restrict__ plan, int queues, int dec_wgs,
-                                                                 PreArgs pa, int pre_items) {
+                                                                 PreArgs pa, int pre_items, int pre_first) {
   using M = MixCfg<HD>;
   __shared__ __attribute__((aligned(16))) char smem[M::LDS];
-  if (static_cast<int>(blockIdx.x) < dec_wgs) {
+  // pre_first = 0: decode workgroups [0, dec_wgs), then the prefill items.  pre_first > 0 (a
+  // multiple of 8, >= pre_items): the prefill items first, in workgroups [0, pre_first), then the
+  // decode workgroups, so the dispatcher places the items before the decode workers take the CUs.
+  const int b = static_cast<int>(blockIdx.x) - pre_first;  // decode workgroup index
+  if (pre_first > 0 ? b >= 0 : b < dec_wgs) {
     // Two decode workers: worker h of workgroup b is worker h * dec_wgs + b of a 2 * dec_wgs grid,
     // so (dec_wgs being a multiple of 8) its index modulo 8 is still its XCD.
     const int half = threadIdx.x >> 8;
@@ -40,11 +44,12 @@ __global__ __launch_bounds__(kPreThreads) void mixed_step_kernel(DecArgs da, con
     if ((threadIdx.x & 255) == 0) tail[4 * half] = 0;
     __syncthreads();  // both halves pass this once, before they go separate ways
     HalfSync sync{tail + 4 * half, 0};
-    decode_worker<HD, CHECK, NARROW, KV8>(da, pieces, plan, queues, half * dec_wgs + static_cast<int>(blockIdx.x),
-                                          2 * dec_wgs, smem + half * M::DEC, tail + 4 * half + 1, sync);
+    decode_worker<HD, CHECK, NARROW, KV8>(da, pieces, plan, queues, half * dec_wgs + b, 2 * dec_wgs,
+                                          smem + half * M::DEC, tail + 4 * half + 1, sync);
   } else {
-    prefill_body<HD, CHECK, NARROW, KV8>(pa, static_cast<int>(blockIdx.x) - dec_wgs, pre_items, smem,
-                                         reinterpret_cast<int*>(smem + PreCfg<HD>::LDS));
+    const int id = pre_first > 0 ? static_cast<int>(blockIdx.x) : b - dec_wgs;
+    if (id < pre_items)
+      prefill_body<HD, CHECK, NARROW, KV8>(pa, id, pre_items, smem, reinterpret_cast<int*>(smem + PreCfg<HD>::LDS));
   }
 }
 
@@ -52,6 +57,24 @@ __global__ __launch_bounds__(kPreThreads) void mixed_step_kernel(DecArgs da, con
 
 using namespace pkv;
 using namespace pkv_dec;
+
+void pkv_dec::launch_prefix_decode(const DecArgs& da, const int2* pieces, int32_t* plan, int queues, int dec_wgs,
+                                   const PreArgs& pa, int pre_items, int32_t head_dim, bool check, bool narrow,
+                                   hipStream_t st) {
+  const int pre_first = (pre_items + 7) / 8 * 8;
+  const unsigned grid = static_cast<unsigned>(pre_first + dec_wgs);
+#define PKV_PXD(HD, CHECK, NARROW)                                                                               \
+  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, false>), dim3(grid), dim3(kPreThreads), 0, st, da, \
+                     pieces, plan, queues, dec_wgs, pa, pre_items, pre_first)
+#define PKV_PXD_N(HD, CHECK) \
+  if (narrow) PKV_PXD(HD, CHECK, true); else PKV_PXD(HD, CHECK, false);
+#define PKV_PXD_C(HD) \
+  if (check) { PKV_PXD_N(HD, true) } else { PKV_PXD_N(HD, false) }
+  if (head_dim == 64) { PKV_PXD_C(64) } else { PKV_PXD_C(128) }
+#undef PKV_PXD_C
+#undef PKV_PXD_N
+#undef PKV_PXD
+}
 
 namespace {
 
@@ -121,7 +144,7 @@ extern "C" pkv_status pkv_paged_attn_mixed(
     ws_ml = max_splits > 1 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr;
     da = DecArgs{static_cast<const uint16_t*>(dec_query), key_pool, value_pool, dec_block_tables, context_lens, ws_o,
                  ws_ml, dec_out, err_flag, dec_max_blocks, num_q_heads, num_kv_heads, group, num_blocks, S,
-                 max_splits, ob, scale_log2, vs, num_dec_seqs};
+                 max_splits, ob, scale_log2, vs, num_dec_seqs, nullptr, 0, max_splits};
     // As many workers as the decode launch has workgroups (two per CU), two per workgroup; the
     // workgroup count is a multiple of 8 so that worker indices keep their XCD.
     const int64_t max_items = static_cast<int64_t>(num_dec_seqs) * num_kv_heads * max_splits;
@@ -161,7 +184,7 @@ extern "C" pkv_status pkv_paged_attn_mixed(
   const unsigned grid = static_cast<unsigned>(dec_wgs + pre_items);
 #define PKV_MIX(HD, CHECK, NARROW, KV8)                                                                   \
   hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, KV8>), dim3(grid), dim3(kPreThreads), 0, st, da, \
-                     pieces, plan, queues, dec_wgs, pa, pre_items)
+                     pieces, plan, queues, dec_wgs, pa, pre_items, 0)
 #define PKV_MIX_K(HD, CHECK, NARROW) \
   if (kv8) PKV_MIX(HD, CHECK, NARROW, true); else PKV_MIX(HD, CHECK, NARROW, false);
 #define PKV_MIX_N(HD, CHECK) \

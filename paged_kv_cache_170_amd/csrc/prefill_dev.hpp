@@ -56,6 +56,13 @@ struct PreArgs {
   int ksplit;
   float* ws_o;   // [row items][ksplit][kPreTile][HD]
   float* ws_ml;  // [row items][ksplit][kPreTile][2]
+  // Shared-prefix mode (prefix_members != null): the rows of KV head g are the pairs (member m,
+  // query head g*G + i) of the decode queries, row m*G + i; the keys are the first prefix_blocks
+  // blocks of member 0's table, all visible; the (o, m, l) partial of a row goes to slot
+  // prefix_slot0 + key split of that query's row in the decode workspace (ws_o / ws_ml with
+  // prefix_slots slots per (sequence, query head)).
+  const int32_t* prefix_members;
+  int num_members, prefix_blocks, prefix_slots, prefix_slot0, prefix_num_seqs;
 };
 
 // One work item (one key split of 256 query rows of one query head) on a 512-thread workgroup.
@@ -85,37 +92,53 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   const int wk = (items % 8 == 0) ? (id % 8) * (items / 8) + id / 8 : id;
   const int kh = wk % ksplit;  // key split
   const int w = wk / ksplit;   // row-tile item
+  const bool prefix = A_.prefix_members != nullptr;
   const int t = w % q_tiles;
   int r = w / q_tiles;
-  const int hi = r % group;
-  r /= group;
+  const int hi = prefix ? 0 : r % group;
+  r = prefix ? r : r / group;
   const int g = r % num_kv_heads;
-  const int s = r / num_kv_heads;
+  const int s = prefix ? A_.prefix_members[0] : r / num_kv_heads;
+  if (prefix && (s < 0 || s >= A_.prefix_num_seqs)) {
+    if (CHECK && threadIdx.x == 0) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+    return;
+  }
   const int h = g * group + hi;
 
-  const int qlo = cu_q_lens[s];
-  const int L = cu_q_lens[s + 1] - qlo;
-  const int off = chunk_offsets[s];
+  const int qlo = prefix ? 0 : cu_q_lens[s];
+  const int L = prefix ? A_.num_members * group : cu_q_lens[s + 1] - qlo;
+  const int off = prefix ? 0 : chunk_offsets[s];
   const int row0 = t * kPreTile;
   if (row0 >= L) return;
   if (off < 0 || static_cast<int64_t>(off) + L > static_cast<int64_t>(max_blocks) * kBlockSize) {
-    if (CHECK && threadIdx.x == 0 && t == 0 && hi == 0) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
-    return;
+    if (!prefix) {
+      if (CHECK && threadIdx.x == 0 && t == 0 && hi == 0) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+      return;
+    }
   }
-  const int kv_end = causal ? off + min(row0 + kPreTile, L) : off + L;
+  const int kv_end = prefix ? A_.prefix_blocks * kBlockSize : causal ? off + min(row0 + kPreTile, L) : off + L;
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int qc = lane & 31, hh = lane >> 5;
   const int wrow0 = row0 + wave * kPreRows;
   const int myrow = wrow0 + qc;
-  const bool row_ok = myrow < L;
-  const int qpos = off + myrow;
   const int32_t* table = block_tables + static_cast<int64_t>(s) * max_blocks;
+  // Shared-prefix mode: this row's decode query (member sequence, query head).
+  int p_seq = prefix && myrow < L ? A_.prefix_members[myrow / group] : 0;
+  if (prefix && (p_seq < 0 || p_seq >= A_.prefix_num_seqs)) {
+    if (CHECK) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
+    p_seq = -1;
+  }
+  const bool row_ok = myrow < L && p_seq >= 0;
+  const int qpos = off + myrow;
+  const int p_head = prefix ? g * group + myrow % group : h;
 
   // Q^T as the B operand: lane (qc, hh) holds query row qc, head_dim 16ks + 8hh .. +7.
   bf16x8 qf[C::KS];
   {
-    const uint16_t* qrow = query + (static_cast<int64_t>(qlo + (row_ok ? myrow : 0)) * num_q_heads + h) * HD + 8 * hh;
+    const int64_t qr = prefix ? static_cast<int64_t>(p_seq) * num_q_heads + p_head
+                              : static_cast<int64_t>(qlo + (row_ok ? myrow : 0)) * num_q_heads + h;
+    const uint16_t* qrow = query + qr * HD + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = row_ok ? as_bf16x8(ld16(qrow + 16 * ks)) : bf16x8{};
   }
@@ -340,6 +363,25 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
 
   // Output.  One split: normalise and write the rows.  Several: see below.
   l_run += __shfl_xor(l_run, 32);
+  if constexpr (HD <= 128) {
+    if (prefix) {
+      // The row's (o, m, l) partial goes to its decode query's prefix slot for this key split.
+      if (!row_ok) return;
+      const int64_t part = (static_cast<int64_t>(p_seq) * num_q_heads + p_head) * A_.prefix_slots + A_.prefix_slot0 + kh;
+      float* my_o = A_.ws_o + part * HD;
+#pragma unroll
+      for (int md = 0; md < C::MD; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 32 * md + 8 * i + 4 * hh;
+          *reinterpret_cast<float4*>(my_o + d) =
+              float4{acc[md][4 * i] * v_scale, acc[md][4 * i + 1] * v_scale, acc[md][4 * i + 2] * v_scale,
+                     acc[md][4 * i + 3] * v_scale};
+        }
+      if (hh == 0) *reinterpret_cast<float2*>(A_.ws_ml + part * 2) = float2{m_ref, l_run};
+      return;
+    }
+  }
   const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
   auto write_rows = [&](float ia) {
 #pragma unroll

@@ -150,7 +150,37 @@ def test_host_validation_rejects_bad_arguments():
     assert sm(null, null, 4, null, null, 0, 5, 10, 16, null, null) == 0
 
 
+def test_shared_prefix_decode_host_checks():
+    import paged_kv_cache_170_amd as pkv
+
+    lib = pkv._lib
+    null = None
+    fake = ctypes.c_void_p(16)
+    pd = lib.pkv_paged_attn_decode_prefix
+
+    def call(num_seqs=4, hd=64, dtype=1, members=fake, num_members=2, prefix_blocks=3, max_blocks=8, ws=fake,
+             ws_bytes=1 << 30, split=0):
+        return pd(fake, 0, fake, fake, fake, fake, max_blocks, fake, num_seqs, 8, 8, hd, 100, 0.1, dtype, members,
+                  num_members, prefix_blocks, split, ws, ws_bytes, null, null)
+
+    assert call(dtype=2) == 2                         # bf16 pools only
+    assert call(hd=256) == 2                          # the prefix items take head_dim 64 or 128
+    assert call(num_members=5) == 1                   # more members than sequences
+    assert call(prefix_blocks=9) == 1                 # prefix longer than a table row
+    assert call(prefix_blocks=-1) == 1
+    assert call(members=null) == 1                    # members needed when there is a prefix
+    assert call(split=100) == 1
+    assert call(ws=null) == 3                         # the workspace is always required
+    assert call(ws_bytes=16) == 3
+    assert call(num_seqs=0, num_members=0) == 0       # empty batch: nothing to do
+    # The shared-prefix workspace holds the plain decode's and the prefix partials and member flags.
+    a = lib.pkv_decode_prefix_workspace_bytes(4, 8, 8, 64, 8, 0)
+    assert a > lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 8, 0) > 0
+    assert lib.pkv_decode_prefix_workspace_bytes(4, 8, 3, 64, 8, 0) == 0
+
+
 @pytest.mark.parametrize("name", ["pkv_cache_write", "pkv_paged_attn_decode", "pkv_paged_attn_prefill_chunk",
+                                  "pkv_paged_attn_decode_prefix",
                                   "pkv_cache_write_fp8", "pkv_paged_attn_decode_fp8",
                                   "pkv_paged_attn_prefill_chunk_fp8"])
 def test_header_documents_each_call(name):

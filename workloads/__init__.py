@@ -326,6 +326,39 @@ def long_decode(poison: bool = False, num_seqs: int = 58, context: int = 4096, w
     return case
 
 
+SHARED_PREFIX_BLOCKS = 256
+
+
+def shared_prefix_decode(poison: bool = False, num_seqs: int = 64, with_data: bool = True) -> PagedCase:
+    """Decode batch behind one cached system prompt, 70B-style GQA (64/8 heads, head_dim 128,
+    bf16): 64 sequences whose logical blocks 0..255 map to the same 256 physical blocks (a shared
+    4,096-token prompt), each followed by a private part uniform in [1, 512] tokens; the pool is
+    the live blocks + 10% free, handed out from a shuffled free list.  Every sequence is a member
+    of the shared prefix (notes["members"], notes["prefix_blocks"])."""
+    rng = np.random.default_rng(6)
+    draw = _Draws(6)
+    hq, hkv, hd = 64, 8, 128
+    P = SHARED_PREFIX_BLOCKS
+    ctx = (P * BLOCK_SIZE + rng.integers(1, 512, size=num_seqs, endpoint=True)).astype(np.int32)
+    need = [math.ceil(int(c) / BLOCK_SIZE) for c in ctx]
+    nblk = math.ceil(1.1 * (P + sum(n - P for n in need)))
+    perm = rng.permutation(nblk).astype(np.int32)
+    shared = perm[:P]
+    bt = allocate_from_free_list(perm[P:], need, max(need), shared_prefix=shared)
+    q = _values(draw, (num_seqs, hq, hd), "bf16", with_data)
+    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    kpool = _values(draw, shape, "bf16", with_data)
+    vpool = _values(draw, shape, "bf16", with_data)
+    case = PagedCase("shared_prefix_decode", "decode", "bf16", hq, hkv, hd, nblk, BLOCK_SIZE, 1.0 / math.sqrt(hd),
+                     ctx, bt, kpool, vpool, np.zeros(num_seqs + 1, np.int32), np.zeros(num_seqs, np.int32),
+                     np.zeros((0, hkv, hd), np.uint16), np.zeros((0, hkv, hd), np.uint16), q,
+                     notes={"shared_blocks": shared.copy(), "prefix_blocks": P,
+                            "members": np.arange(num_seqs, dtype=np.int32)})
+    if poison and with_data:
+        _poison_dead_slots(case, ctx)
+    return case
+
+
 MIXED_PREFIX_BLOCKS = 63
 MIXED_PROMPT = 32768
 MIXED_CHUNK = 512
