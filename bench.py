@@ -75,14 +75,15 @@ def sources_hash(names):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel_key: str, src: str):
-    """HBM bytes per launch from a committed counter summary, if it was taken on these sources."""
+def counter_traffic(kernel_key: str, src):
+    """HBM bytes per launch from a committed counter summary, if it was taken on these sources
+    (src: one .hip file or a list of them)."""
     path = os.path.join(PROFILES, f"counters_{kernel_key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("sources_hash") != sources_hash([src]):
+    if rec.get("sources_hash") != sources_hash([src] if isinstance(src, str) else list(src)):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -415,7 +416,9 @@ def main():
     if args.cold_steps > 0:
         secondary["kernel_ms_cold"] = {n: spread(cold[n]) for n in ran}
         secondary["decode_gbs_unique_cold"] = dec_bytes / (float(np.median(cold["decode"])) * 1e-3) / 1e9
-    kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs, HBM_PEAK_GBS, "GB/s", "decode.hip")}
+    # The shared-prefix decode also runs the fused launch (mixed.hip) and the prefill body.
+    dec_src = ["decode.hip", "mixed.hip", "prefill.hip"] if pfx else "decode.hip"
+    kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs, HBM_PEAK_GBS, "GB/s", dec_src)}
     if pre is not None:
         fl = prefill_flops(pre)
         pre_tf = fl / (avg_ms["prefill"] * 1e-3) / 1e12
