@@ -65,7 +65,7 @@ def run_mode(pkv, torch, mode, args, prompt, output, arrival):
     for p, o, a in zip(prompt, output, arrival):
         sched.add_request(int(p), int(o), float(a))
     g = torch.Generator(device=dev).manual_seed(args.seed)
-    kp = torch.zeros((nblk, 16, hkv, hd), dtype=torch.bfloat16, device=dev)
+    kp = torch.zeros((nblk, hkv, 16, hd), dtype=torch.bfloat16, device=dev)
     vp = torch.zeros_like(kp)
     # Synthetic step inputs: slices of fixed random buffers (contents do not affect timing).
     max_tok = max(args.token_budget, int(prompt.max())) * (1 if mode == 3 else args.max_running) + args.max_running

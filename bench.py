@@ -182,9 +182,11 @@ def main():
     if fp8:
         kp8 = torch.empty(kp.shape, dtype=torch.float8_e4m3fn, device=dev)
         vp8 = torch.empty_like(kp8)
-        nrow = kp.shape[0] * kp.shape[1]
+        nrow = kp.shape[0] * kp.shape[2]
         all_slots = torch.arange(nrow, dtype=torch.int32, device=dev)
-        pkv.cache_write_fp8(kp.view(nrow, kp.shape[2], kp.shape[3]), vp.view(nrow, vp.shape[2], vp.shape[3]), kp8, vp8,
+        # Token rows in slot order (pools are [blocks, Hkv, 16, hd]) through the quantising write.
+        rows = lambda p: p.permute(0, 2, 1, 3).reshape(nrow, p.shape[1], p.shape[3])
+        pkv.cache_write_fp8(rows(kp), rows(vp), kp8, vp8,
                             all_slots, k_scale, v_scale)
         torch.cuda.synchronize()
         del all_slots

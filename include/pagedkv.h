@@ -25,9 +25,11 @@
  *                     shared block is copied only when one of them writes into it.
  *
  * Data layout shared by every call (all device memory, caller-owned):
- *   key_pool, value_pool  [num_blocks, 16, num_kv_heads, head_dim], row-major, same dtype.  A
- *                         "slot" is one token row of num_kv_heads*head_dim elements at flat row
- *                         index block*16 + offset.
+ *   key_pool, value_pool  [num_blocks, num_kv_heads, 16, head_dim], row-major, same dtype: the
+ *                         pages' pool of blocks x 16 x (num_kv_heads*head_dim) with each block's
+ *                         16 rows grouped by KV head, so that one KV head's share of a block is a
+ *                         contiguous run of 16*head_dim elements.  A "slot" block*16 + offset holds
+ *                         one token: its row of KV head h is [block][h][offset][:].
  *   block_tables          int32 [num_seqs, max_blocks_per_seq], row-major.  Entry [s][j] is the
  *                         physical block of sequence s's tokens 16j..16j+15.  Entries past the
  *                         sequence's last live block are never read and may hold anything.
@@ -216,7 +218,7 @@ size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_len, int32_t 
  * FP8 KV pool.  The pages run their model in FP8 ([vLLM-internals], opening benchmark and memory
  * section) without saying how a cache would be stored in it; these calls keep K and V pools of
  * E4M3 codes, one fp32 scale per pool (k_scale, v_scale > 0, finite), so that a code c stands for
- * value(c) * scale.  Pools are [num_blocks, 16, num_kv_heads, head_dim] bytes, token-major as for
+ * value(c) * scale.  Pools are [num_blocks, num_kv_heads, 16, head_dim] bytes, laid out as for
  * the other dtypes; slot mapping, block tables, the gather and the block copy are unchanged.
  *
  * Cache write with quantisation: for t < num_tokens with slot = slot_mapping[t] >= 0, every

@@ -95,21 +95,21 @@ def quantize_bf16_bits(bits: np.ndarray, scale: float) -> np.ndarray:
 
 def cache_write_fp8(key_pool: np.ndarray, value_pool: np.ndarray, key_f32: np.ndarray, value_f32: np.ndarray,
                     slots: np.ndarray, k_scale: float, v_scale: float):
-    """Copies of the code pools ``[N_blk, 16, Hkv, hd]`` (uint8) with token ``t``'s quantised K and
-    V rows stored at flat row ``slots[t]``; negative slots are skipped, slots must be unique."""
-    nblk, b, hkv, hd = key_pool.shape
+    """Copies of the code pools ``[N_blk, Hkv, 16, hd]`` (uint8) with token ``t``'s quantised K and
+    V rows stored at slot ``slots[t]`` (its block, its offset, every KV head); negative slots are
+    skipped, slots must be unique."""
+    nblk, hkv, b, hd = key_pool.shape
     live = slots[slots >= 0]
     if live.size and live.max() >= nblk * b:
         raise ValueError("slot outside the pool")
     if np.unique(live).size != live.size:
         raise ValueError("duplicate slots")
     kp, vp = key_pool.copy(), value_pool.copy()
-    krows, vrows = kp.reshape(nblk * b, hkv * hd), vp.reshape(nblk * b, hkv * hd)
     for t, sl in enumerate(slots):
         if sl < 0:
             continue
-        krows[sl] = quantize(key_f32[t].reshape(-1), k_scale)
-        vrows[sl] = quantize(value_f32[t].reshape(-1), v_scale)
+        kp[sl // b, :, sl % b] = quantize(key_f32[t].reshape(-1), k_scale).reshape(hkv, hd)
+        vp[sl // b, :, sl % b] = quantize(value_f32[t].reshape(-1), v_scale).reshape(hkv, hd)
     return kp, vp
 
 

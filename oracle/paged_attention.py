@@ -29,8 +29,10 @@ Sources (cited by page title and section):
 
 Readings where the pages are silent (each is listed in the design notes):
 
-* pool layout is token-major ``[num_blocks, block_size, Hkv, hd]``; a slot is
-  one row of ``Hkv*hd`` elements at flat index ``block*block_size + offset``;
+* pool layout is ``[num_blocks, Hkv, block_size, hd]``: the page's pool of
+  blocks x block size x D with each block's rows grouped by KV head; a slot
+  ``block*block_size + offset`` holds one token, whose row of KV head ``g`` is
+  ``pool[block, g, offset]``;
 * query head ``h`` uses KV head ``h // (Hq // Hkv)``;
 * ``context_lens`` counts the current token, so decode attends to
   positions ``[0, ctx)``; ``ctx == 0`` gives a zero row;
@@ -91,13 +93,14 @@ def slot_mapping(block_tables: np.ndarray, cu_new_lens: np.ndarray, start_pos: n
 
 def cache_write(key_pool: np.ndarray, value_pool: np.ndarray, key: np.ndarray, value: np.ndarray,
                 slots: np.ndarray):
-    """Return copies of the pools with token ``t``'s K and V rows stored at flat row ``slots[t]``.
+    """Return copies of the pools with token ``t``'s K and V rows stored at slot ``slots[t]``
+    (block ``slot // block_size``, offset ``slot % block_size``, every KV head).
 
     The copy is exact (same storage type, bit for bit).  Negative slots are skipped.  Slots must
     be unique and inside the pool ([Chunked-Prefill]: prefill stores the K/V it computes in the
     cache, which grows block by block).
     """
-    nblk, b, hkv, hd = key_pool.shape
+    nblk, hkv, b, hd = key_pool.shape
     live = slots[slots >= 0]
     if live.size and (live.max() >= nblk * b):
         raise ValueError("slot outside the pool")
@@ -105,13 +108,11 @@ def cache_write(key_pool: np.ndarray, value_pool: np.ndarray, key: np.ndarray, v
         raise ValueError("duplicate slots")
     kp = key_pool.copy()
     vp = value_pool.copy()
-    krows = kp.reshape(nblk * b, hkv * hd)
-    vrows = vp.reshape(nblk * b, hkv * hd)
     for t, sl in enumerate(slots):
         if sl < 0:
             continue
-        krows[sl] = key[t].reshape(-1)
-        vrows[sl] = value[t].reshape(-1)
+        kp[sl // b, :, sl % b] = key[t]
+        vp[sl // b, :, sl % b] = value[t]
     return kp, vp
 
 
@@ -120,11 +121,12 @@ def gather(pool: np.ndarray, block_table_row: np.ndarray, length: int) -> np.nda
     blocks named by the first ``ceil(length / block_size)`` table entries, concatenated in
     logical order and cut to ``length`` rows ([C13-L2] figure "按块表取 K").  Later table entries
     are never read."""
-    b = pool.shape[1]
+    _, hkv, b, hd = pool.shape
     nb = -(-int(length) // b)
     if nb == 0:
-        return pool[:0].reshape((0,) + pool.shape[2:])
-    blocks = [pool[int(block_table_row[j])] for j in range(nb)]
+        return np.zeros((0, hkv, hd), pool.dtype)
+    # Block j as [token, Hkv, hd] rows: its [Hkv, token, hd] array with the two axes swapped.
+    blocks = [pool[int(block_table_row[j])].transpose(1, 0, 2) for j in range(nb)]
     return np.concatenate(blocks, axis=0)[:length]
 
 
@@ -172,7 +174,7 @@ def decode(query: np.ndarray, key_pool: np.ndarray, value_pool: np.ndarray, bloc
     from the query's."""
     kv_dtype = kv_dtype or dtype
     B, hq, hd = query.shape
-    hkv = key_pool.shape[2]
+    hkv = key_pool.shape[1]
     q = as_f64(query, dtype)
     out = np.zeros((B, hq, hd), dtype=np.float64)
     for s in range(B):
@@ -200,7 +202,7 @@ def prefill_chunk(query: np.ndarray, cu_q_lens: np.ndarray, chunk_offsets: np.nd
     """
     kv_dtype = kv_dtype or dtype
     total, hq, hd = query.shape
-    hkv = key_pool.shape[2]
+    hkv = key_pool.shape[1]
     out = np.zeros((total, hq, hd), dtype=np.float64)
     want = None if rows is None else set(int(r) for r in rows)
     for s in range(len(chunk_offsets)):
@@ -235,7 +237,7 @@ def decode_split_partials(query: np.ndarray, key_pool: np.ndarray, value_pool: n
     ``exp(score - m)``, ``o`` = sum of ``exp(score - m) * v``.  Returns a dict keyed by
     ``(s, h)`` of ``(o [n_split, hd], m [n_split], l [n_split])``."""
     B, hq, hd = query.shape
-    hkv = key_pool.shape[2]
+    hkv = key_pool.shape[1]
     q = as_f64(query, dtype)
     res = {}
     for s in range(B):

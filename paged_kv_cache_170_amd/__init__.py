@@ -6,8 +6,8 @@ point of the same name.  All computation happens in the HIP kernels.  The
 library is loaded on import; if it has not been built, the import fails
 loudly (there is no fallback).
 
-Tensors: pools are ``[num_blocks, 16, num_kv_heads, head_dim]`` (K and V
-separate, same dtype); block tables, context lengths, slot mappings and
+Tensors: pools are ``[num_blocks, num_kv_heads, 16, head_dim]`` (K and V
+separate, same dtype: each block's 16 token rows grouped by KV head); block tables, context lengths, slot mappings and
 offsets are int32 device tensors.  FP8 pools hold E4M3 codes as
 ``torch.float8_e4m3fn`` (or ``torch.uint8``) tensors and come with one fp32
 scale per pool (the ``*_fp8`` calls).
@@ -142,10 +142,10 @@ def _need_i32(*ts):
 
 def _pool_dims(key_pool: torch.Tensor, value_pool: torch.Tensor):
     if key_pool.shape != value_pool.shape or key_pool.dtype != value_pool.dtype or key_pool.dim() != 4:
-        raise ValueError("key_pool and value_pool must both be [num_blocks, 16, num_kv_heads, head_dim], same dtype")
+        raise ValueError("key_pool and value_pool must both be [num_blocks, num_kv_heads, 16, head_dim], same dtype")
     if not (key_pool.is_contiguous() and value_pool.is_contiguous()):
         raise ValueError("pools must be contiguous")
-    nblk, bs, hkv, hd = key_pool.shape
+    nblk, hkv, bs, hd = key_pool.shape
     return nblk, bs, hkv, hd
 
 

@@ -37,14 +37,17 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(int32_t* __restrict__
 }
 
 // Row copy: each thread moves one VEC-byte piece of one token's K row and V row.  Rows are
-// `row_bytes` long; VEC divides row_bytes and the alignment of every address.
+// `row_bytes` long (head_bytes per KV head, each head's piece going to its own run of the block);
+// VEC divides head_bytes and the alignment of every address.
 template <int VEC, bool CHECK>
 __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict__ key, const char* __restrict__ value,
                                                           int64_t key_stride_bytes, int64_t value_stride_bytes,
                                                           char* __restrict__ key_pool, char* __restrict__ value_pool,
                                                           const int32_t* __restrict__ slots, int num_tokens,
-                                                          int row_bytes, int64_t num_slots, int32_t* err_flag) {
+                                                          int row_bytes, int head_bytes, int64_t num_slots,
+                                                          int32_t* err_flag) {
   const int pieces = row_bytes / VEC;
+  const int num_kv_heads = row_bytes / head_bytes;
   const int64_t total = static_cast<int64_t>(num_tokens) * pieces;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const char* __restrict
       if (c == 0) atomicOr(err_flag, PKV_FLAG_BAD_SLOT);
       continue;
     }
-    const int64_t dst = static_cast<int64_t>(slot) * row_bytes + static_cast<int64_t>(c) * VEC;
+    const int64_t dst = pool_slot_byte(slot, c * VEC, head_bytes, num_kv_heads);
     const char* ks = key + t * key_stride_bytes + c * VEC;
     const char* vs = value + t * value_stride_bytes + c * VEC;
     if constexpr (VEC == 16) {
@@ -102,9 +105,10 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(const T* __restric
                                                               uint8_t* __restrict__ key_pool,
                                                               uint8_t* __restrict__ value_pool,
                                                               const int32_t* __restrict__ slots, int num_tokens,
-                                                              int row_elems, int64_t num_slots, float inv_k,
-                                                              float inv_v, int32_t* err_flag) {
+                                                              int row_elems, int head_dim, int64_t num_slots,
+                                                              float inv_k, float inv_v, int32_t* err_flag) {
   const int pieces = row_elems / 8;
+  const int num_kv_heads = row_elems / head_dim;
   const int64_t total = static_cast<int64_t>(num_tokens) * pieces;
   auto widen = [](T v) -> float {
     if constexpr (sizeof(T) == 2) return bf16_to_f32(v); else return v;
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(const T* __restric
       if (c == 0) atomicOr(err_flag, PKV_FLAG_BAD_SLOT);
       continue;
     }
-    const int64_t dst = static_cast<int64_t>(slot) * row_elems + static_cast<int64_t>(c) * 8;
+    const int64_t dst = pool_slot_byte(slot, c * 8, head_dim, num_kv_heads);  // one byte per code
     *reinterpret_cast<uint2*>(key_pool + dst) = codes8(key + t * key_stride + c * 8, inv_k);
     *reinterpret_cast<uint2*>(value_pool + dst) = codes8(value + t * value_stride + c * 8, inv_v);
   }
@@ -196,8 +200,11 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(char* __restrict__ ke
   const int b = load_block_id<CHECK>(block_tables + static_cast<int64_t>(s) * max_blocks, t >> 4, num_blocks,
                                      err_flag);
   if (b < 0) return;
-  // Same row arithmetic as the attention kernels (KV head 0 starts the whole token row).
-  const int64_t src = pool_row_offset(b, t & (kBlockSize - 1), num_kv_heads, 0, head_dim) * elem_bytes + c * 16;
+  // Same row arithmetic as the attention kernels: piece c lies in KV head h's row of the token.
+  const int head_bytes = head_dim * elem_bytes;
+  const int h = c * 16 / head_bytes;
+  const int64_t src = pool_row_offset(b, t & (kBlockSize - 1), num_kv_heads, h, head_dim) * elem_bytes +
+                      (c * 16 - h * head_bytes);
   const int64_t dst = (static_cast<int64_t>(cu_out[s]) + t) * row_bytes + c * 16;
   st16(key_out + dst, ld16(key_pool + src));
   st16(value_out + dst, ld16(value_pool + src));
@@ -262,7 +269,8 @@ extern "C" pkv_status pkv_cache_write(const void* key, const void* value, int64_
 #define PKV_LAUNCH_WRITE(V, C)                                                                                   \
   hipLaunchKernelGGL((cache_write_kernel<V, C>), dim3(blocks), dim3(256), 0, st, static_cast<const char*>(key),  \
                      static_cast<const char*>(value), ks, vs, static_cast<char*>(key_pool),                      \
-                     static_cast<char*>(value_pool), slot_mapping, num_tokens, row_bytes, num_slots, err_flag)
+                     static_cast<char*>(value_pool), slot_mapping, num_tokens, row_bytes, head_dim * e, num_slots, \
+                     err_flag)
   if (vec == 16) {
     if (err_flag) PKV_LAUNCH_WRITE(16, true); else PKV_LAUNCH_WRITE(16, false);
   } else if (vec == 4) {
@@ -303,7 +311,7 @@ extern "C" pkv_status pkv_cache_write_fp8(const void* key, const void* value, in
   hipLaunchKernelGGL((cache_write_fp8_kernel<T, V, C>), dim3(blocks), dim3(256), 0, st,                         \
                      static_cast<const T*>(key), static_cast<const T*>(value), key_tok_stride, value_tok_stride, \
                      static_cast<uint8_t*>(key_pool), static_cast<uint8_t*>(value_pool), slot_mapping,          \
-                     num_tokens, static_cast<int>(row_elems), num_slots, inv_k, inv_v, err_flag)
+                     num_tokens, static_cast<int>(row_elems), head_dim, num_slots, inv_k, inv_v, err_flag)
 #define PKV_LAUNCH_W8_C(T, V) \
   if (err_flag) PKV_LAUNCH_W8(T, V, true); else PKV_LAUNCH_W8(T, V, false);
   if (in_dtype == PKV_DTYPE_BF16) {

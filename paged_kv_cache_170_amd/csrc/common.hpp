@@ -21,13 +21,23 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------------------------
-// Pool addressing.  A pool is [num_blocks, 16, num_kv_heads, head_dim]; a token's row for one KV
-// head starts at ((block * 16 + offset) * num_kv_heads + kv_head) * head_dim elements.
+// Pool addressing.  A pool is [num_blocks, num_kv_heads, 16, head_dim]: inside a block the 16
+// token rows of one KV head are contiguous (head_dim * 16 elements), so a KV head's share of a
+// block is one contiguous run.  The row of (block, offset, kv_head) starts at
+// ((block * num_kv_heads + kv_head) * 16 + offset) * head_dim elements.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ int64_t pool_row_offset(int block, int offset, int num_kv_heads, int kv_head,
                                                    int head_dim) {
-  return ((static_cast<int64_t>(block) * kBlockSize + offset) * num_kv_heads + kv_head) *
+  return ((static_cast<int64_t>(block) * num_kv_heads + kv_head) * kBlockSize + offset) *
          static_cast<int64_t>(head_dim);
+}
+
+// Byte offset, inside a pool, of byte w of a token's full K (or V) row (all KV heads, head_bytes
+// per head, head-major inside the row) once written to `slot`.
+__device__ __forceinline__ int64_t pool_slot_byte(int64_t slot, int w, int head_bytes, int num_kv_heads) {
+  const int h = w / head_bytes;
+  return ((slot / kBlockSize * num_kv_heads + h) * kBlockSize + slot % kBlockSize) * head_bytes +
+         (w - h * head_bytes);
 }
 
 // Byte offset of (block, in-block offset c_bytes) in a pool whose blocks are blk_bytes long.  With

@@ -200,8 +200,9 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   // Step u covers positions tok0 + 32u .. +31 (two blocks).  K and V rows are read whole (each
   // wave-wide load covers RPL complete rows) and staged in LDS in their natural layout.
   const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * E);
-  const uint32_t row_bytes = static_cast<uint32_t>(num_kv_heads * HD * E);
-  const uint32_t c0 = static_cast<uint32_t>((row_base * num_kv_heads + g) * HD * E + col * E);
+  // The KV head's 16 rows of a block are one contiguous run (head-major blocks).
+  const uint32_t row_bytes = static_cast<uint32_t>(HD * E);
+  const uint32_t c0 = static_cast<uint32_t>((g * kBlockSize + row_base) * HD * E + col * E);
   auto load = [&](int u, DecBuf<HD, E>& B) {
     const int t0 = tok0 + 32 * u;
     // Blocks 2u and 2u + 1 of the split (u is the same across the wave).

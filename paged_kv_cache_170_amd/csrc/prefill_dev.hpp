@@ -166,7 +166,7 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   constexpr int RPI = kPreThreads / C::CPR;  // pair rows per load round
   const int t_row = threadIdx.x / C::CPR;
   const uint32_t blk_bytes = static_cast<uint32_t>(kBlockSize * num_kv_heads * HD * E);
-  const uint32_t c0 = static_cast<uint32_t>(((t_row % kBlockSize) * num_kv_heads + g) * HD * E + (threadIdx.x % C::CPR) * 16);
+  const uint32_t c0 = static_cast<uint32_t>((g * kBlockSize + t_row % kBlockSize) * HD * E + (threadIdx.x % C::CPR) * 16);
   uint4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_pair = [&](int p) {
     const int key0p = 2 * p * C::KT + t_row;

@@ -57,10 +57,10 @@ def codes_of(t):
 def quantised_pools(pkv, c, dev, err):
     """FP8 pools of a bf16 case: every slot of its bf16 pools quantised by the GPU write, checked
     byte for byte against the oracle's quantisation."""
-    nblk, b, hkv, hd = c.key_pool.shape
-    rows_k = c.key_pool.reshape(nblk * b, hkv, hd)
-    rows_v = c.value_pool.reshape(nblk * b, hkv, hd)
-    kp = torch.zeros((nblk, b, hkv, hd), dtype=torch.float8_e4m3fn, device=dev)
+    nblk, hkv, b, hd = c.key_pool.shape
+    rows_k = wl.slot_rows(c.key_pool)
+    rows_v = wl.slot_rows(c.value_pool)
+    kp = torch.zeros((nblk, hkv, b, hd), dtype=torch.float8_e4m3fn, device=dev)
     vp = torch.zeros_like(kp)
     slots = torch.arange(nblk * b, dtype=torch.int32, device=dev)
     pkv.cache_write_fp8(to_dev(rows_k, dev, True), to_dev(rows_v, dev, True), kp, vp, slots, K_SCALE, V_SCALE,
@@ -118,8 +118,8 @@ def test_quantising_write_bit_exact_special_values(pkv, dev):
             assert xin.stride(0) == 2 * hkv * hd
             slots = rng.permutation(nblk * 16)[:T].astype(np.int32)
             slots[::7] = -1
-            kp0 = rng.integers(0, 256, (nblk, 16, hkv, hd), dtype=np.uint8)
-            vp0 = rng.integers(0, 256, (nblk, 16, hkv, hd), dtype=np.uint8)
+            kp0 = rng.integers(0, 256, (nblk, hkv, 16, hd), dtype=np.uint8)
+            vp0 = rng.integers(0, 256, (nblk, hkv, 16, hd), dtype=np.uint8)
             kp, vp = to_dev(kp0, dev).view(torch.float8_e4m3fn), to_dev(vp0, dev).view(torch.float8_e4m3fn)
             err = torch.zeros(1, dtype=torch.int32, device=dev)
             pkv.cache_write_fp8(xin, xin, kp, vp, to_dev(slots, dev), scale, V_SCALE, err_flag=err)
@@ -137,16 +137,16 @@ def test_one_key_decode_returns_dequantised_values(pkv, dev):
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
     n_seq = 8
     row = np.resize(codes, (n_seq, hkv * hd))
-    vp0 = np.zeros((n_seq, 16, hkv, hd), np.uint8)
-    vp0[:, 0] = row.reshape(n_seq, hkv, hd)
+    vp0 = np.zeros((n_seq, hkv, 16, hd), np.uint8)
+    vp0[:, :, 0] = row.reshape(n_seq, hkv, hd)  # offset 0 of each block, every KV head
     rng = np.random.default_rng(2)
-    kp0 = rng.integers(0, 0x70, (n_seq, 16, hkv, hd), dtype=np.uint8)  # finite K codes
+    kp0 = rng.integers(0, 0x70, (n_seq, hkv, 16, hd), dtype=np.uint8)  # finite K codes
     kp, vp = to_dev(kp0, dev).view(torch.float8_e4m3fn), to_dev(vp0, dev).view(torch.float8_e4m3fn)
     q = to_dev(wl.f32_to_bf16_bits(rng.standard_normal((n_seq, hq, hd)).astype(np.float32)), dev, True)
     bt = to_dev(np.arange(n_seq, dtype=np.int32)[:, None], dev)
     ctx = to_dev(np.ones(n_seq, np.int32), dev)
     out = pkv.paged_attn_decode_fp8(q, kp, vp, bt, ctx, hd ** -0.5, K_SCALE, V_SCALE).cpu().numpy()
-    want = ofp8.dequantize(vp0[:, 0], V_SCALE)  # [n_seq, hkv, hd]
+    want = ofp8.dequantize(vp0[:, :, 0], V_SCALE)  # [n_seq, hkv, hd]
     for h in range(hq):
         assert np.array_equal(out[:, h].astype(np.float64), want[:, oracle.kv_head_of(h, hq, hkv)])
 
@@ -257,11 +257,11 @@ def test_fp8_mixed_step_full_size(pkv, dev):
     _say("case fp8 mixed step: 127 decode sequences + 512-row chunk at 16,384, 64/8 x 128, E4M3 pools")
     dec, pre = wl.mixed_step(poison=True)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    nblk, b, hkv, hd = pre.key_pool.shape
-    kp = torch.empty((nblk, b, hkv, hd), dtype=torch.float8_e4m3fn, device=dev)
+    nblk, hkv, b, hd = pre.key_pool.shape
+    kp = torch.empty((nblk, hkv, b, hd), dtype=torch.float8_e4m3fn, device=dev)
     vp = torch.empty_like(kp)
-    pkv.cache_write_fp8(to_dev(pre.key_pool.reshape(nblk * b, hkv, hd), dev, True),
-                        to_dev(pre.value_pool.reshape(nblk * b, hkv, hd), dev, True), kp, vp,
+    pkv.cache_write_fp8(to_dev(wl.slot_rows(pre.key_pool), dev, True),
+                        to_dev(wl.slot_rows(pre.value_pool), dev, True), kp, vp,
                         torch.arange(nblk * b, dtype=torch.int32, device=dev), K_SCALE, V_SCALE, err_flag=err)
     rk = ofp8.quantize_bf16_bits(pre.key_pool, K_SCALE)
     rv = ofp8.quantize_bf16_bits(pre.value_pool, V_SCALE)

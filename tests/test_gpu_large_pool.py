@@ -114,18 +114,19 @@ def test_pools_past_4gib_bit_identical(pkv, fp8):
     dq = to_dev(dq_host, dev, True)
     # Small pools: the case as generated; large pools: the same blocks at id + base.
     pool_dtype = torch.float8_e4m3fn if fp8 else torch.bfloat16
-    shape = (c.num_blocks, 16, HKV, HD)
+    shape = (c.num_blocks, HKV, 16, HD)
     k16, v16 = to_dev(c.key_pool, dev, True), to_dev(c.value_pool, dev, True)
     if fp8:
         # Both pools hold the quantised case (written by the library's own FP8 write).
         n = c.num_blocks * 16
         ks = torch.empty(shape, dtype=pool_dtype, device=dev)
         vs = torch.empty_like(ks)
-        pkv.cache_write_fp8(k16.view(n, HKV, HD), v16.view(n, HKV, HD), ks, vs,
+        pkv.cache_write_fp8(k16.permute(0, 2, 1, 3).reshape(n, HKV, HD), v16.permute(0, 2, 1, 3).reshape(n, HKV, HD),
+                            ks, vs,
                             torch.arange(n, dtype=torch.int32, device=dev), 0.0123, 2.0 ** -5)
     else:
         ks, vs = k16, v16
-    kb = torch.empty((nbig, 16, HKV, HD), dtype=pool_dtype, device=dev)
+    kb = torch.empty((nbig, HKV, 16, HD), dtype=pool_dtype, device=dev)
     vb = torch.empty_like(kb)
     ids = torch.arange(base, base + c.num_blocks, dtype=torch.int64, device=dev)
     kb.view(torch.uint8).index_copy_(0, ids, ks.view(torch.uint8))

@@ -135,7 +135,9 @@ def test_fused_random_batches(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, fp8):
         n = c.num_blocks * 16
         kp8 = torch.empty(kp.shape, dtype=torch.float8_e4m3fn, device=dev)
         vp8 = torch.empty_like(kp8)
-        pkv.cache_write_fp8(kp.view(n, hkv, hd), vp.view(n, hkv, hd), kp8, vp8,
+        # Every slot's token row (the pools are [blocks, Hkv, 16, hd]) through the quantising write.
+        pkv.cache_write_fp8(kp.permute(0, 2, 1, 3).reshape(n, hkv, hd), vp.permute(0, 2, 1, 3).reshape(n, hkv, hd),
+                            kp8, vp8,
                             torch.arange(n, dtype=torch.int32, device=dev), *scales, err_flag=err)
         kp, vp = kp8, vp8
         rk = ofp8.dequantize(ofp8.quantize_bf16_bits(rk, scales[0]), scales[0])

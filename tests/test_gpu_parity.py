@@ -325,13 +325,13 @@ def test_decode_edge_contexts(pkv, dev, ctx_list):
     nblk = sum(need) + 2
     free = np.random.default_rng(5).permutation(nblk).astype(np.int32)
     bt = wl.allocate_from_free_list(free, need, max(need) + 1)
-    shape = (nblk, 16, 2, 128)
+    shape = (nblk, 2, 16, 128)
     rng = np.random.default_rng(6)
     kp = wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
     vp = wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
     live = wl.live_slot_mask(bt, ctx, nblk)
-    kp[~live] = wl.BF16_NAN_BITS
-    vp[~live] = wl.BF16_NAN_BITS
+    wl.set_slots(kp, ~live, wl.BF16_NAN_BITS)
+    wl.set_slots(vp, ~live, wl.BF16_NAN_BITS)
     c2 = wl.PagedCase(**{**c.__dict__, "key_pool": kp, "value_pool": vp, "block_tables": bt, "context_lens": ctx,
                          "num_blocks": nblk})
     d = Dev(c2, dev)
@@ -489,8 +489,8 @@ def test_copy_blocks_bit_exact(pkv, dev):
     _say("case copy_blocks: 300 of 1,000 bf16 blocks (8 x 128) copied, whole pools compared")
     rng = np.random.default_rng(11)
     nblk, hkv, hd = 1000, 8, 128
-    kp = _bf16_bits(rng, (nblk, 16, hkv, hd))
-    vp = _bf16_bits(rng, (nblk, 16, hkv, hd))
+    kp = _bf16_bits(rng, (nblk, hkv, 16, hd))
+    vp = _bf16_bits(rng, (nblk, hkv, 16, hd))
     perm = rng.permutation(nblk).astype(np.int32)
     src, dst = perm[:300].copy(), perm[300:600].copy()
     src[:5] = dst[:5]  # src == dst: no-op
@@ -521,7 +521,7 @@ def test_block_manager_prefix_cache_and_copy_on_write_decode(pkv, dev):
     rng = np.random.default_rng(12)
     hq, hkv, hd, nblk, maxb = 16, 4, 128, 256, 32
     bm = pkv.BlockManager(nblk, free_order=rng.permutation(nblk).astype(np.int32))
-    kp = torch.full((nblk, 16, hkv, hd), float("nan"), dtype=torch.bfloat16, device=dev)
+    kp = torch.full((nblk, hkv, 16, hd), float("nan"), dtype=torch.bfloat16, device=dev)
     vp = torch.full_like(kp, float("nan"))
     err = new_err(dev)
     sys_tok = rng.integers(0, 30000, 100)

@@ -121,7 +121,7 @@ def shared_prefix_case(seed, hq, hkv, hd, P, num_seqs, member_ctx, other_ctx):
         cursor += private[s]
         bt[s, :len(row)] = row
     f32 = lambda shape: wl.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
-    kpool, vpool = f32((nblk, 16, hkv, hd)), f32((nblk, 16, hkv, hd))
+    kpool, vpool = f32((nblk, hkv, 16, hd)), f32((nblk, hkv, 16, hd))
     q = f32((num_seqs, hq, hd))
     # NaN in every slot no sequence may read: the tails of last blocks and the spare blocks.
     nan = np.uint16(0x7FC0)
@@ -132,8 +132,8 @@ def shared_prefix_case(seed, hq, hkv, hd, P, num_seqs, member_ctx, other_ctx):
         tail = int(ctx[s]) % 16
         if tail:
             b = bt[s, nb - 1]
-            kpool[b, tail:] = nan
-            vpool[b, tail:] = nan
+            kpool[b, :, tail:] = nan
+            vpool[b, :, tail:] = nan
     for b in range(nblk):
         if b not in used:
             kpool[b] = nan

@@ -54,10 +54,10 @@ def test_block_table_example_engine_core_page():
 def test_gather_small_scale_instance():
     g = _golden("p2_gather_small.json")
     nblk, b, D = g["num_blocks"], g["block_size"], g["D"]
-    pool = np.zeros((nblk, b, 1, D), np.float32)
+    pool = np.zeros((nblk, 1, b, D), np.float32)  # [blocks, KV heads, block size, D]
     for blk in range(nblk):
         for s in range(b):
-            pool[blk, s, 0] = 100 * blk + 10 * s + np.arange(D)
+            pool[blk, 0, s] = 100 * blk + 10 * s + np.arange(D)
     row = np.array(g["block_table"], np.int32)
     got6 = oracle.gather(pool, row, 6)[:, 0]
     got5 = oracle.gather(pool, row, 5)[:, 0]
@@ -80,11 +80,11 @@ def test_write_then_gather_round_trip_is_bit_exact(block_size, storage):
     if storage == "f32":
         seq_k = rng.integers(0, 2 ** 32, size=(n, hkv, hd), dtype=np.uint64).astype(np.uint32).view(np.float32)
         seq_v = rng.integers(0, 2 ** 32, size=(n, hkv, hd), dtype=np.uint64).astype(np.uint32).view(np.float32)
-        pool = np.zeros((nblk, block_size, hkv, hd), np.float32)
+        pool = np.zeros((nblk, hkv, block_size, hd), np.float32)
     else:
         seq_k = rng.integers(0, 2 ** 16, size=(n, hkv, hd)).astype(np.uint16)
         seq_v = rng.integers(0, 2 ** 16, size=(n, hkv, hd)).astype(np.uint16)
-        pool = np.zeros((nblk, block_size, hkv, hd), np.uint16)
+        pool = np.zeros((nblk, hkv, block_size, hd), np.uint16)
     slots = oracle.slot_mapping(row[None, :], np.array([0, n], np.int32), np.array([0], np.int32), block_size)
     kp, vp = oracle.cache_write(pool, pool, seq_k, seq_v, slots)
     assert oracle.gather(kp, row, n).tobytes() == seq_k.tobytes()
@@ -93,13 +93,13 @@ def test_write_then_gather_round_trip_is_bit_exact(block_size, storage):
     skip = slots.copy()
     skip[::2] = -1
     kp2, _ = oracle.cache_write(pool, pool, seq_k, seq_v, skip)
-    flat = kp2.reshape(nblk * block_size, -1)
+    flat = kp2.transpose(0, 2, 1, 3).reshape(nblk * block_size, -1)  # one token row per slot
     assert (flat[slots[::2]] == 0).all()
     assert flat[slots[1::2]].tobytes() == seq_k[1::2].reshape(len(slots[1::2]), -1).tobytes()
 
 
 def test_cache_write_rejects_bad_slots():
-    pool = np.zeros((2, 16, 1, 4), np.float32)
+    pool = np.zeros((2, 1, 16, 4), np.float32)
     k = np.ones((2, 1, 4), np.float32)
     with pytest.raises(ValueError):
         oracle.cache_write(pool, pool, k, k, np.array([3, 3], np.int32))
@@ -145,8 +145,8 @@ def test_gqa_decode_matches_torch_sdpa_enable_gqa():
     for s in range(c.num_seqs):
         n = int(c.context_lens[s])
         # Contiguous K/V assembled directly from pool rows named by the table, without oracle.gather.
-        rows_k = np.stack([c.key_pool[c.block_tables[s, p // 16], p % 16] for p in range(n)]).astype(np.float64)
-        rows_v = np.stack([c.value_pool[c.block_tables[s, p // 16], p % 16] for p in range(n)]).astype(np.float64)
+        rows_k = np.stack([c.key_pool[c.block_tables[s, p // 16], :, p % 16] for p in range(n)]).astype(np.float64)
+        rows_v = np.stack([c.value_pool[c.block_tables[s, p // 16], :, p % 16] for p in range(n)]).astype(np.float64)
         q = c.query[s].astype(np.float64)[:, None, :]
         ref = _sdpa(q, rows_k.transpose(1, 0, 2), rows_v.transpose(1, 0, 2), c.scale, gqa=True)
         np.testing.assert_allclose(got[s], ref[:, 0], rtol=0, atol=1e-12)
@@ -212,7 +212,7 @@ def test_page_example_fp32_prints_true():
     vn = v[0].permute(1, 0, 2).contiguous().numpy()
     nb = -(-n // 16)
     bt = np.arange(nb, dtype=np.int32)[None, :]
-    pool = np.zeros((nb, 16, g["heads"], hd), np.float32)
+    pool = np.zeros((nb, g["heads"], 16, hd), np.float32)
     slots = oracle.slot_mapping(bt, np.array([0, n], np.int32), np.array([0], np.int32), 16)
     kp, vp = oracle.cache_write(pool, pool, kn, vn, slots)
     got = oracle.prefill_chunk(qn, np.array([0, n], np.int32), np.array([0], np.int32), kp, vp, bt,
@@ -243,7 +243,7 @@ def test_decimal_bruteforce_decode_and_prefill(seed):
     v = rng.standard_normal((n, hkv, hd)).astype(np.float32)
     q = (rng.standard_normal((1, hq, hd)) * 2).astype(np.float32)
     bt = np.array([[1]], np.int32)
-    pool = np.zeros((2, 16, hkv, hd), np.float32)
+    pool = np.zeros((2, hkv, 16, hd), np.float32)
     kp, vp = oracle.cache_write(pool, pool, k, v, np.arange(16, 16 + n, dtype=np.int32))
     scale = 1.0 / math.sqrt(hd)
     got = oracle.decode(q, kp, vp, bt, np.array([n], np.int32), scale, "f32")
@@ -268,7 +268,7 @@ def test_decimal_bruteforce_decode_and_prefill(seed):
 def test_closed_forms():
     rng = np.random.default_rng(5)
     hd = 8
-    pool = np.zeros((4, 16, 1, hd), np.float32)
+    pool = np.zeros((4, 1, 16, hd), np.float32)
     v = rng.standard_normal((40, 1, hd)).astype(np.float32)
     k = rng.standard_normal((40, 1, hd)).astype(np.float32)
     bt = np.array([[2, 0, 3]], np.int32)
@@ -332,8 +332,8 @@ def test_gqa_equals_repeated_mha():
     c = wl.random_case(51, kind="decode", dtype="f32", num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=16,
                        max_ctx=60, min_ctx=1, new_tokens=False, poison=False)
     G = 4
-    kp = np.repeat(c.key_pool, G, axis=2)
-    vp = np.repeat(c.value_pool, G, axis=2)
+    kp = np.repeat(c.key_pool, G, axis=1)  # the KV-head axis of [blocks, Hkv, 16, hd]
+    vp = np.repeat(c.value_pool, G, axis=1)
     a = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "f32")
     b = oracle.decode(c.query, kp, vp, c.block_tables, c.context_lens, c.scale, "f32")
     assert np.max(np.abs(a - b)) <= 1e-13
@@ -390,7 +390,7 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
         orig = pa.gather
 
         def reversed_blocks(pool, row, length):
-            b = pool.shape[1]
+            b = pool.shape[2]
             nb = -(-int(length) // b)
             return orig(pool, np.concatenate([row[:nb][::-1], row[nb:]]), length)
         monkeypatch.setattr(pa, "gather", reversed_blocks)

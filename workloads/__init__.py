@@ -8,11 +8,13 @@ returns and compute everything else on their own.
 
 Storage conventions (shared by both sides because they are the *inputs*):
 
-* The KV pool of one layer is ``[num_blocks, block_size, num_kv_heads,
-  head_dim]``, token-major inside a block, K and V in separate pools.  This
-  is the pool drawn in "C13 推理 · 第2课 服务端" (geekvape-learning), section
-  "改进二:PagedAttention", figure "按块表取 K" and its dimension table
-  (pool = blocks x block size x D, D = KV heads x head dim).
+* The KV pool of one layer is ``[num_blocks, num_kv_heads, block_size,
+  head_dim]``, K and V in separate pools: the pool drawn in "C13 推理 · 第2课
+  服务端" (geekvape-learning), section "改进二:PagedAttention", figure "按块表取
+  K" and its dimension table (pool = blocks x block size x D, D = KV heads x
+  head dim), with each block's rows grouped by KV head.  Slot
+  ``block * block_size + offset`` holds one token; its row of KV head g is
+  ``pool[block, g, offset]``.
 * bf16 values are carried as ``uint16`` bit patterns, produced from fp32
   draws with round-to-nearest-even.  fp32 values are plain ``float32``.
 * Block tables are ``int32 [num_seqs, max_blocks_per_seq]``; entries past a
@@ -189,12 +191,24 @@ def live_slot_mask(block_tables: np.ndarray, lens: np.ndarray, num_blocks: int,
     return mask
 
 
+def slot_rows(pool: np.ndarray) -> np.ndarray:
+    """The pool's token rows in slot order, ``[num_blocks * block_size, Hkv, hd]`` (a copy)."""
+    nblk, hkv, b, hd = pool.shape
+    return np.ascontiguousarray(pool.transpose(0, 2, 1, 3)).reshape(nblk * b, hkv, hd)
+
+
+def set_slots(pool: np.ndarray, mask: np.ndarray, value) -> None:
+    """Store ``value`` in every element of the slots ``mask`` (bool [num_blocks, block_size])
+    selects, for every KV head: pools are [num_blocks, Hkv, block_size, hd]."""
+    pool.transpose(0, 2, 1, 3)[mask] = value
+
+
 def _poison_dead_slots(case: PagedCase, live_lens: np.ndarray) -> None:
     live = live_slot_mask(case.block_tables, live_lens, case.num_blocks, case.block_size)
     dead = ~live
     p = _poison_value(case.dtype)
-    case.key_pool[dead] = p
-    case.value_pool[dead] = p
+    set_slots(case.key_pool, dead, p)
+    set_slots(case.value_pool, dead, p)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -225,7 +239,7 @@ def tiny_decode(poison: bool = True, with_data: bool = True) -> PagedCase:
     bt = allocate_from_free_list(free, need, max(need))
     T = int(ctx.sum())
     q = _values(draw, (4, hq, hd), "f32", with_data)
-    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    shape = (nblk, hkv, BLOCK_SIZE, hd)
     kpool = np.full(shape, np.nan if poison else 0.0, dtype=np.float32)
     knew = _values(draw, (T, hkv, hd), "f32", with_data)
     vpool = np.full(shape, np.nan if poison else 0.0, dtype=np.float32)
@@ -254,7 +268,7 @@ def chunked_prefill(poison: bool = True, prompt_len: int = 1000, chunk: int = 25
     free = rng.permutation(nblk).astype(np.int32)
     bt = allocate_from_free_list(free, [need], need)
     q = _values(draw, (prompt_len, hq, hd), "bf16", with_data)
-    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    shape = (nblk, hkv, BLOCK_SIZE, hd)
     fill = BF16_NAN_BITS if poison else np.uint16(0)
     kpool = np.full(shape, fill, dtype=np.uint16)
     knew = _values(draw, (prompt_len, hkv, hd), "bf16", with_data)
@@ -286,7 +300,7 @@ def gqa_decode(poison: bool = False, num_seqs: int = 128, with_data: bool = True
     free = rng.permutation(nblk).astype(np.int32)
     bt = allocate_from_free_list(free, need, 8192 // BLOCK_SIZE)
     q = _values(draw, (num_seqs, hq, hd), "bf16", with_data)
-    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    shape = (nblk, hkv, BLOCK_SIZE, hd)
     kpool = _values(draw, shape, "bf16", with_data)
     vpool = _values(draw, shape, "bf16", with_data)
     case = PagedCase("gqa_decode", "decode", "bf16", hq, hkv, hd, nblk, BLOCK_SIZE, 1.0 / math.sqrt(hd),
@@ -311,7 +325,7 @@ def long_decode(poison: bool = False, num_seqs: int = 58, context: int = 4096, w
     bt = perm.reshape(num_seqs, per).copy()
     new_per = BLOCK_SIZE
     q = _values(draw, (num_seqs, hq, hd), "bf16", with_data)
-    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    shape = (nblk, hkv, BLOCK_SIZE, hd)
     kpool = _values(draw, shape, "bf16", with_data)
     knew = _values(draw, (num_seqs * new_per, hkv, hd), "bf16", with_data)
     vpool = _values(draw, shape, "bf16", with_data)
@@ -346,7 +360,7 @@ def shared_prefix_decode(poison: bool = False, num_seqs: int = 64, with_data: bo
     shared = perm[:P]
     bt = allocate_from_free_list(perm[P:], need, max(need), shared_prefix=shared)
     q = _values(draw, (num_seqs, hq, hd), "bf16", with_data)
-    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    shape = (nblk, hkv, BLOCK_SIZE, hd)
     kpool = _values(draw, shape, "bf16", with_data)
     vpool = _values(draw, shape, "bf16", with_data)
     case = PagedCase("shared_prefix_decode", "decode", "bf16", hq, hkv, hd, nblk, BLOCK_SIZE, 1.0 / math.sqrt(hd),
@@ -390,7 +404,7 @@ def mixed_step(poison: bool = False, num_decode: int = 127, with_data: bool = Tr
     bt_pre[0, :pre_blocks] = pre_ids
     q_dec = _values(draw, (num_decode, hq, hd), "bf16", with_data)
     q_pre = _values(draw, (MIXED_CHUNK, hq, hd), "bf16", with_data)
-    shape = (nblk, BLOCK_SIZE, hkv, hd)
+    shape = (nblk, hkv, BLOCK_SIZE, hd)
     kpool = _values(draw, shape, "bf16", with_data)
     knew = _values(draw, (MIXED_CHUNK, hkv, hd), "bf16", with_data)
     vpool = _values(draw, shape, "bf16", with_data)
@@ -408,8 +422,8 @@ def mixed_step(poison: bool = False, num_decode: int = 127, with_data: bool = Tr
     if poison and with_data:
         live = live_slot_mask(bt_dec, ctx, nblk) | live_slot_mask(bt_pre, np.array([MIXED_OFFSET]), nblk)
         dead = ~live
-        kpool[dead] = BF16_NAN_BITS
-        vpool[dead] = BF16_NAN_BITS
+        set_slots(kpool, dead, BF16_NAN_BITS)
+        set_slots(vpool, dead, BF16_NAN_BITS)
     return dec, pre
 
 
@@ -437,7 +451,7 @@ def random_case(seed: int, *, kind: str, dtype: str, num_seqs: int, num_q_heads:
     bt = allocate_from_free_list(free, need, max(1, max(need) + 1))
     nq = num_seqs if kind == "decode" else int(qlen.sum())
     q = draw((nq, num_q_heads, head_dim), dtype)
-    shape = (nblk, BLOCK_SIZE, num_kv_heads, head_dim)
+    shape = (nblk, num_kv_heads, BLOCK_SIZE, head_dim)
     T = int(newl.sum())
     kpool = draw(shape, dtype)
     knew = draw((T, num_kv_heads, head_dim), dtype)
