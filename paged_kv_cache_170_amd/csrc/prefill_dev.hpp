@@ -136,7 +136,7 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   // Q^T as the B operand: lane (qc, hh) holds query row qc, head_dim 16ks + 8hh .. +7.
   bf16x8 qf[C::KS];
   {
-    const int64_t qr = prefix ? static_cast<int64_t>(p_seq) * num_q_heads + p_head
+    const int64_t qr = prefix ? static_cast<int64_t>(row_ok ? p_seq : 0) * num_q_heads + p_head
                               : static_cast<int64_t>(qlo + (row_ok ? myrow : 0)) * num_q_heads + h;
     const uint16_t* qrow = query + qr * HD + 8 * hh;
 #pragma unroll

@@ -189,3 +189,21 @@ def test_no_members_is_the_plain_decode(pkv):
     b = pkv.paged_attn_decode(q, kp, vp, bt, ctx, c.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_bad_member_index_is_flagged_and_skipped(pkv):
+    """A member index outside [0, num_seqs) (not the first) sets the bad-length flag in checked
+    mode and is skipped; every sequence's output is still the oracle's."""
+    dev = torch.device("cuda:0")
+    hq, hkv, hd, P = 16, 2, 128, 9
+    _say("case prefix decode: an out-of-range member index")
+    q, kpool, vpool, bt, ctx, members = shared_prefix_case(99, hq, hkv, hd, P, 6, [144, 400, 1000], [0, 300, 37])
+    bad = np.concatenate([members, np.array([6 + 5], np.int32)])
+    kp, vp = to_dev(kpool, dev, True), to_dev(vpool, dev, True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    scale = hd ** -0.5
+    out = pkv.paged_attn_decode_prefix(to_dev(q, dev, True), kp, vp, to_dev(bt, dev), to_dev(ctx, dev), scale,
+                                       to_dev(bad, dev), P, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & pkv.FLAG_BAD_LENGTH
+    close(out.cpu().numpy(), oracle.decode(q, kpool, vpool, bt, ctx, scale, "bf16"), "prefix decode vs oracle")
