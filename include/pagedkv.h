@@ -265,7 +265,24 @@ pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtype, const vo
                                         int32_t split_tokens, void* workspace, size_t workspace_bytes,
                                         int32_t* err_flag, void* stream);
 
-/* Workspace bytes of pkv_paged_attn_decode_prefix for these shapes (0 for unsupported shapes). */
+/*
+ * Shared-prefix decode over FP8 pools ([Engine-core] §1.5 and §3.2, as pkv_paged_attn_decode_prefix;
+ * the pools as for pkv_paged_attn_decode_fp8): computes what pkv_paged_attn_decode_fp8 computes
+ * (attention over the dequantised values, bf16 queries) with the shared prefix attended once per
+ * KV head.  k_scale, v_scale: the pools' scales (> 0, finite; PKV_ERR_INVALID_ARG otherwise).  Other
+ * arguments, the workspace (pkv_decode_prefix_workspace_bytes) and the errors as for
+ * pkv_paged_attn_decode_prefix; head_dim 64 or 128.
+ */
+pkv_status pkv_paged_attn_decode_prefix_fp8(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                            const void* value_pool, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t num_blocks, float scale, float k_scale,
+                                            float v_scale, const int32_t* prefix_members, int32_t num_members,
+                                            int32_t prefix_blocks, int32_t split_tokens, void* workspace,
+                                            size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+/* Workspace bytes of pkv_paged_attn_decode_prefix(_fp8) for these shapes (0 for unsupported shapes). */
 size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_blocks_per_seq, int32_t split_tokens);
 

@@ -45,6 +45,8 @@ _SIGS = {
     "pkv_decode_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attn_decode_prefix": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _f32, _i32, _vp, _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_paged_attn_decode_prefix_fp8": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                _i32, _f32, _f32, _f32, _vp, _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                      _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -475,6 +477,40 @@ def paged_attn_decode_prefix(query: torch.Tensor, key_pool: torch.Tensor, value_
                                              int(prefix_blocks), int(split_tokens), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _ptr(err_flag),
                                              _stream(query.device)), "pkv_paged_attn_decode_prefix")
+    return out
+
+
+def paged_attn_decode_prefix_fp8(query: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float, k_scale: float,
+                                 v_scale: float, prefix_members: torch.Tensor, prefix_blocks: int,
+                                 out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                                 workspace: torch.Tensor | None = None, split_tokens: int = 0,
+                                 err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """Shared-prefix decode over E4M3 pools; see pkv_paged_attn_decode_prefix_fp8."""
+    _need_gpu(query, key_pool, value_pool, block_tables, context_lens, prefix_members, out, workspace, err_flag)
+    _need_i32(block_tables, context_lens, prefix_members, err_flag)
+    if prefix_members.dim() != 1 or not prefix_members.is_contiguous():
+        raise ValueError("prefix_members must be a contiguous 1-D int32 tensor")
+    nblk, bs, hkv, hd = _need_fp8_pools(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != torch.bfloat16 or not query.is_contiguous():
+        raise ValueError("query must be contiguous bf16 [num_seqs, num_q_heads, head_dim]")
+    B, hq, _ = query.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((B, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (B, hq, hd):
+        raise ValueError("out must be contiguous [num_seqs, num_q_heads, head_dim]")
+    if workspace is None:
+        workspace = decode_prefix_workspace(query, hkv, block_tables.shape[1], split_tokens)
+    _check(_lib.pkv_paged_attn_decode_prefix_fp8(_ptr(out), _dtype_code(out), _ptr(query), _ptr(key_pool),
+                                                 _ptr(value_pool), _ptr(block_tables), block_tables.shape[1],
+                                                 _ptr(context_lens), B, hq, hkv, hd, nblk, float(scale),
+                                                 float(k_scale), float(v_scale), _ptr(prefix_members),
+                                                 prefix_members.shape[0], int(prefix_blocks), int(split_tokens),
+                                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                 _ptr(err_flag), _stream(query.device)),
+           "pkv_paged_attn_decode_prefix_fp8")
     return out
 
 

@@ -560,16 +560,18 @@ extern "C" size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t nu
   return pfx_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, S).total;
 }
 
-extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtype, const void* query,
-                                                   const void* key_pool, const void* value_pool,
-                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                                   const int32_t* context_lens, int32_t num_seqs,
-                                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                                   int32_t num_blocks, float scale, pkv_dtype dtype,
-                                                   const int32_t* prefix_members, int32_t num_members,
-                                                   int32_t prefix_blocks, int32_t split_tokens, void* workspace,
-                                                   size_t workspace_bytes, int32_t* err_flag, void* stream) {
-  if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+namespace {
+
+// Body of the bf16 and FP8 shared-prefix calls (dtype = pool dtype; queries are bf16; the scales
+// are 1 for bf16 pools).
+pkv_status decode_prefix_impl(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                              const void* value_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, float scale, pkv_dtype dtype,
+                              float k_scale, float v_scale, const int32_t* prefix_members, int32_t num_members,
+                              int32_t prefix_blocks, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                              int32_t* err_flag, void* stream) {
+  const bool kv8 = dtype == PKV_DTYPE_FP8_E4M3;
   if (out_dtype != PKV_DTYPE_F32 && out_dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_members < 0 || prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq || num_members > num_seqs)
@@ -590,9 +592,14 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtyp
   if (!workspace || workspace_bytes < lay.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
   // No shared prefix: the ordinary decode (its layout fits in this one).
   if (num_members == 0 || prefix_blocks == 0)
-    return pkv_paged_attn_decode(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq,
-                                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale,
-                                 dtype, S, workspace, workspace_bytes, err_flag, stream);
+    return kv8 ? pkv_paged_attn_decode_fp8(out, out_dtype, query, key_pool, value_pool, block_tables,
+                                           max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                           head_dim, num_blocks, scale, k_scale, v_scale, S, workspace,
+                                           workspace_bytes, err_flag, stream)
+               : pkv_paged_attn_decode(out, out_dtype, query, key_pool, value_pool, block_tables,
+                                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                       head_dim, num_blocks, scale, dtype, S, workspace, workspace_bytes, err_flag,
+                                       stream);
   if (static_cast<int64_t>(num_seqs) * lay.max_splits * num_kv_heads > INT32_MAX / 2) return PKV_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
   int32_t* plan = reinterpret_cast<int32_t*>(ws);
@@ -601,12 +608,13 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtyp
   float* ws_ml = reinterpret_cast<float*>(ws + lay.base.ml);
   uint8_t* member = reinterpret_cast<uint8_t*>(ws + lay.member);
   const int group = num_q_heads / num_kv_heads;
-  const float scale_log2 = scale * kLog2e;
+  const float scale_log2 = scale * kLog2e * k_scale;  // the K scale folds into the exponent
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool check = err_flag != nullptr;
-  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * 2 < (1ull << 32) &&
-                      num_blocks < (1 << 24);
+  const bool narrow =
+      static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) < (1ull << 32) &&
+      num_blocks < (1 << 24);
 
   // Prefix pass: rows (member, query head) of each KV head, key splits of the prefix.
   const int q_tiles = static_cast<int>((static_cast<int64_t>(num_members) * group + kPreTile - 1) / kPreTile);
@@ -629,7 +637,7 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtyp
   pa.num_blocks = num_blocks;
   pa.causal = 0;
   pa.scale_log2 = scale_log2;
-  pa.v_scale = 1.f;
+  pa.v_scale = v_scale;
   pa.err_flag = err_flag;
   pa.ksplit = kp;
   pa.ws_o = ws_o;
@@ -657,12 +665,48 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtyp
   // partial), then the reduce merges both.
   const DecArgs a{static_cast<const uint16_t*>(query), key_pool, value_pool, block_tables, context_lens, ws_o, ws_ml,
                   out, err_flag, max_blocks_per_seq, num_q_heads, num_kv_heads, group, num_blocks, S, lay.max_splits,
-                  ob, scale_log2, 1.f, num_seqs, member, prefix_blocks, lay.slots};
+                  ob, scale_log2, v_scale, num_seqs, member, prefix_blocks, lay.slots};
   const int64_t pre_items = row_items * kp;
   if (pre_items + dec_wgs + 8 > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
-  launch_prefix_decode(a, pieces, plan, queues, dec_wgs, pa, static_cast<int>(pre_items), head_dim, check, narrow, st);
+  launch_prefix_decode(a, pieces, plan, queues, dec_wgs, pa, static_cast<int>(pre_items), head_dim, check, narrow,
+                       kv8, st);
   if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
   launch_reduce(ws_o, ws_ml, context_lens, max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, S,
                 lay.slots, out, ob, st, member, prefix_blocks, lay.max_splits, kp);
   return pkv_host::launch_status();
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attn_decode_prefix(void* out, pkv_dtype out_dtype, const void* query,
+                                                   const void* key_pool, const void* value_pool,
+                                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                   const int32_t* context_lens, int32_t num_seqs,
+                                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                   int32_t num_blocks, float scale, pkv_dtype dtype,
+                                                   const int32_t* prefix_members, int32_t num_members,
+                                                   int32_t prefix_blocks, int32_t split_tokens, void* workspace,
+                                                   size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  if (dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  return decode_prefix_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq,
+                            context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale, dtype,
+                            1.f, 1.f, prefix_members, num_members, prefix_blocks, split_tokens, workspace,
+                            workspace_bytes, err_flag, stream);
+}
+
+extern "C" pkv_status pkv_paged_attn_decode_prefix_fp8(void* out, pkv_dtype out_dtype, const void* query,
+                                                       const void* key_pool, const void* value_pool,
+                                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                       const int32_t* context_lens, int32_t num_seqs,
+                                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                       int32_t num_blocks, float scale, float k_scale, float v_scale,
+                                                       const int32_t* prefix_members, int32_t num_members,
+                                                       int32_t prefix_blocks, int32_t split_tokens, void* workspace,
+                                                       size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  if (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f))
+    return PKV_ERR_INVALID_ARG;
+  return decode_prefix_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq,
+                            context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale,
+                            PKV_DTYPE_FP8_E4M3, k_scale, v_scale, prefix_members, num_members, prefix_blocks,
+                            split_tokens, workspace, workspace_bytes, err_flag, stream);
 }

@@ -476,9 +476,9 @@ void launch_plan(bool check, const int32_t* context_lens, int num_seqs, int max_
                  uint8_t* member_out = nullptr);
 // Launch the shared-prefix decode (mixed.hip): the prefix items (prefill kernel in shared-prefix
 // mode, pre_items workgroups) first, then dec_wgs workgroups of two decode workers each, in one
-// launch; head_dim 64 or 128, bf16 pools.
+// launch; head_dim 64 or 128, bf16 or (kv8) E4M3 pools.
 void launch_prefix_decode(const pkv::DecArgs& da, const int2* pieces, int32_t* plan, int queues, int dec_wgs,
-                          const pkv::PreArgs& pa, int pre_items, int32_t head_dim, bool check, bool narrow,
+                          const pkv::PreArgs& pa, int pre_items, int32_t head_dim, bool check, bool narrow, bool kv8,
                           hipStream_t st);
 // Launch the split reduce (decode.hip).
 // slots: partial slots per (sequence, query head); member / prefix_blocks / prefix_slot0 /

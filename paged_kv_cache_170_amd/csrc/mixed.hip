@@ -60,19 +60,22 @@ using namespace pkv_dec;
 
 void pkv_dec::launch_prefix_decode(const DecArgs& da, const int2* pieces, int32_t* plan, int queues, int dec_wgs,
                                    const PreArgs& pa, int pre_items, int32_t head_dim, bool check, bool narrow,
-                                   hipStream_t st) {
+                                   bool kv8, hipStream_t st) {
   const int pre_first = (pre_items + 7) / 8 * 8;
   const unsigned grid = static_cast<unsigned>(pre_first + dec_wgs);
-#define PKV_PXD(HD, CHECK, NARROW)                                                                               \
-  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, false>), dim3(grid), dim3(kPreThreads), 0, st, da, \
+#define PKV_PXD(HD, CHECK, NARROW, KV8)                                                                        \
+  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, KV8>), dim3(grid), dim3(kPreThreads), 0, st, da,   \
                      pieces, plan, queues, dec_wgs, pa, pre_items, pre_first)
+#define PKV_PXD_K(HD, CHECK, NARROW) \
+  if (kv8) PKV_PXD(HD, CHECK, NARROW, true); else PKV_PXD(HD, CHECK, NARROW, false);
 #define PKV_PXD_N(HD, CHECK) \
-  if (narrow) PKV_PXD(HD, CHECK, true); else PKV_PXD(HD, CHECK, false);
+  if (narrow) { PKV_PXD_K(HD, CHECK, true) } else { PKV_PXD_K(HD, CHECK, false) }
 #define PKV_PXD_C(HD) \
   if (check) { PKV_PXD_N(HD, true) } else { PKV_PXD_N(HD, false) }
   if (head_dim == 64) { PKV_PXD_C(64) } else { PKV_PXD_C(128) }
 #undef PKV_PXD_C
 #undef PKV_PXD_N
+#undef PKV_PXD_K
 #undef PKV_PXD
 }
 

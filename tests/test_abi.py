@@ -173,6 +173,11 @@ def test_shared_prefix_decode_host_checks():
     assert call(ws=null) == 3                         # the workspace is always required
     assert call(ws_bytes=16) == 3
     assert call(num_seqs=0, num_members=0) == 0       # empty batch: nothing to do
+    pd8 = lib.pkv_paged_attn_decode_prefix_fp8
+    args8 = lambda ks, vs: (fake, 0, fake, fake, fake, fake, 8, fake, 4, 8, 8, 64, 100, 0.1, ks, vs, fake, 2, 3, 0,
+                            fake, 1 << 30, null, null)
+    assert pd8(*args8(0.0, 1.0)) == 1                 # scales must be positive and finite
+    assert pd8(*args8(1.0, float("inf"))) == 1
     # The shared-prefix workspace holds the plain decode's and the prefix partials and member flags.
     a = lib.pkv_decode_prefix_workspace_bytes(4, 8, 8, 64, 8, 0)
     assert a > lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 8, 0) > 0
@@ -180,7 +185,7 @@ def test_shared_prefix_decode_host_checks():
 
 
 @pytest.mark.parametrize("name", ["pkv_cache_write", "pkv_paged_attn_decode", "pkv_paged_attn_prefill_chunk",
-                                  "pkv_paged_attn_decode_prefix",
+                                  "pkv_paged_attn_decode_prefix", "pkv_paged_attn_decode_prefix_fp8",
                                   "pkv_cache_write_fp8", "pkv_paged_attn_decode_fp8",
                                   "pkv_paged_attn_prefill_chunk_fp8"])
 def test_header_documents_each_call(name):

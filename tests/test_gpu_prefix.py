@@ -207,3 +207,34 @@ def test_bad_member_index_is_flagged_and_skipped(pkv):
     torch.cuda.synchronize()
     assert int(err.item()) & pkv.FLAG_BAD_LENGTH
     close(out.cpu().numpy(), oracle.decode(q, kpool, vpool, bt, ctx, scale, "bf16"), "prefix decode vs oracle")
+
+
+@pytest.mark.parametrize("hq,hkv,hd,P,mctx,octx,split", [PREFIX_CASES[0], PREFIX_CASES[2], PREFIX_CASES[3]])
+def test_shared_prefix_fp8_pools(pkv, hq, hkv, hd, P, mctx, octx, split):
+    """E4M3 pools (quantised by the library's own write): the shared-prefix decode against the oracle
+    over the dequantised pools and against the plain FP8 decode."""
+    from oracle import fp8 as ofp8
+    dev = torch.device("cuda:0")
+    _say(f"case prefix decode fp8: hq={hq} hkv={hkv} hd={hd} P={P} members={len(mctx)} others={len(octx)}")
+    n = len(mctx) + len(octx)
+    q, kpool, vpool, bt, ctx, members = shared_prefix_case(hq * 5 + hd + P, hq, hkv, hd, P, n, mctx, octx)
+    ks, vs = 2.0 ** -5, 0.0123
+    nblk = kpool.shape[0]
+    kp = torch.empty(kpool.shape, dtype=torch.float8_e4m3fn, device=dev)
+    vp = torch.empty_like(kp)
+    pkv.cache_write_fp8(to_dev(wl.slot_rows(kpool), dev, True), to_dev(wl.slot_rows(vpool), dev, True), kp, vp,
+                        torch.arange(nblk * 16, dtype=torch.int32, device=dev), ks, vs)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    qd, btd, ctxd = to_dev(q, dev, True), to_dev(bt, dev), to_dev(ctx, dev)
+    scale = hd ** -0.5
+    out = pkv.paged_attn_decode_prefix_fp8(qd, kp, vp, btd, ctxd, scale, ks, vs, to_dev(members, dev), P,
+                                           split_tokens=split, err_flag=err)
+    plain = pkv.paged_attn_decode_fp8(qd, kp, vp, btd, ctxd, scale, ks, vs, split_tokens=split, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    rk = ofp8.dequantize(ofp8.quantize_bf16_bits(kpool, ks), ks)
+    rv = ofp8.dequantize(ofp8.quantize_bf16_bits(vpool, vs), vs)
+    mx, mean = close(out.cpu().numpy(), oracle.decode(q, rk, rv, bt, ctx, scale, "bf16", kv_dtype="f64"),
+                     "fp8 prefix decode vs oracle")
+    _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert float((out - plain).abs().max()) <= 5e-3
