@@ -16,7 +16,7 @@ host on the same inputs (decode of every sequence, prefill of a sample of rows).
 
 Other workloads (--workload): gqa_decode and long_decode (decode only), and shared_prefix (64
 sequences behind one 4,096-token cached prompt, decoded by the shared-prefix decode, with the
-plain decode on the same inputs timed beside it).
+plain decode on the same inputs timed beside it; with --kv fp8 the FP8 variants of both).
 """
 from __future__ import annotations
 
@@ -197,8 +197,6 @@ def main():
     # Shared-prefix workload: the decode attends the shared blocks once for all members.
     pfx = args.workload == "shared_prefix"
     if pfx:
-        if fp8:
-            raise SystemExit("the shared-prefix decode takes bf16 pools")
         d_members = to_dev(dec.notes["members"])
         pfx_blocks = int(dec.notes["prefix_blocks"])
         ws = pkv.decode_prefix_workspace(d_q, dec.num_kv_heads, dec.max_blocks_per_seq)
@@ -238,7 +236,10 @@ def main():
             else:
                 pkv.cache_write(w_k, w_v, kp, vp, slots)
         mark(2)
-        if fp8:
+        if fp8 and pfx:
+            pkv.paged_attn_decode_prefix_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, d_members,
+                                             pfx_blocks, out=d_out, workspace=ws)
+        elif fp8:
             pkv.paged_attn_decode_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, out=d_out, workspace=ws)
         elif pfx:
             pkv.paged_attn_decode_prefix(d_q, kp, vp, d_bt, d_ctx, dec.scale, d_members, pfx_blocks, out=d_out,
@@ -347,11 +348,18 @@ def main():
         p_out = torch.empty_like(d_out)
         pws = pkv.decode_workspace(d_q, dec.num_kv_heads, dec.max_blocks_per_seq)
         pt = 1e9
+
+        def plain():
+            if fp8:
+                pkv.paged_attn_decode_fp8(d_q, kp8, vp8, d_bt, d_ctx, dec.scale, k_scale, v_scale, out=p_out,
+                                          workspace=pws)
+            else:
+                pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=p_out, workspace=pws)
         for _ in range(3):
-            pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=p_out, workspace=pws)
+            plain()
             e0.record(stream)
             for _ in range(10):
-                pkv.paged_attn_decode(d_q, kp, vp, d_bt, d_ctx, dec.scale, out=p_out, workspace=pws)
+                plain()
             e1.record(stream)
             torch.cuda.synchronize()
             pt = min(pt, e0.elapsed_time(e1) / 10)
