@@ -52,6 +52,54 @@ def requests(n, seed, rate):
     return prompt, output, arrival
 
 
+def step_layout(plan):
+    """Host-side layout of one planned step's new tokens: every decode entry writes one token (at
+    position ctx - 1), then every prompt chunk writes its tokens; the step's queries are packed in
+    the same order.  Returns (table rows, tokens per entry, first position per entry, cu offsets)."""
+    nd = len(plan["dec_row"])
+    rows = np.concatenate([plan["dec_row"], plan["chunk_row"]]).astype(np.int64)
+    lens = np.concatenate([np.ones(nd, np.int32), plan["chunk_len"]]).astype(np.int32)
+    starts = np.concatenate([plan["dec_ctx"] - 1, plan["chunk_offset"]]).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return rows, lens, starts, cu
+
+
+def run_step(pkv, torch, kp, vp, table, plan, query, key_new, value_new, workspace, scale, err_flag=None,
+             stream=None, events=None):
+    """Execute one planned step on the GPU: slot mapping of the step's new tokens (step_layout's
+    order) through the scheduler's table rows, the cache write of their K/V, then one fused
+    attention launch of the step's decode tokens and prompt chunks (causal).
+
+    table: the scheduler's block-table rows on the device (int32 [max_running, max_blocks]);
+    query [T, Hq, hd], key_new / value_new [T, Hkv, hd] (bf16, T = the step's token count).
+    events: optional (start, end) CUDA events recorded around the GPU work on `stream`.
+    Returns (slots, decode output or None, chunk output or None); outputs are fp32."""
+    dev = kp.device
+    nd, nc = len(plan["dec_row"]), len(plan["chunk_row"])
+    rows, lens, starts, cu = step_layout(plan)
+    T = int(cu[-1])
+    bt_all = table.index_select(0, torch.from_numpy(rows).to(dev))
+    cu_d, st_d = torch.from_numpy(cu).to(dev), torch.from_numpy(starts).to(dev)
+    dec_kw, pre_kw = {}, {}
+    if nd:
+        dec_kw = dict(dec_query=query[:nd], dec_block_tables=bt_all[:nd],
+                      context_lens=torch.from_numpy(plan["dec_ctx"]).to(dev), workspace=workspace)
+    if nc:
+        ccu = np.concatenate([[0], np.cumsum(plan["chunk_len"])]).astype(np.int32)
+        pre_kw = dict(pre_query=query[nd:nd + int(ccu[-1])], cu_q_lens=torch.from_numpy(ccu).to(dev),
+                      chunk_offsets=torch.from_numpy(plan["chunk_offset"]).to(dev),
+                      pre_block_tables=bt_all[nd:], max_q_len=int(plan["chunk_len"].max()))
+    slots = torch.empty(T, dtype=torch.int32, device=dev)
+    if events is not None:
+        events[0].record(stream)
+    pkv.slot_mapping(bt_all, cu_d, st_d, int(lens.max()), kp.shape[0], out=slots, err_flag=err_flag)
+    pkv.cache_write(key_new[:T], value_new[:T], kp, vp, slots, err_flag=err_flag)
+    dec_out, pre_out = pkv.paged_attn_mixed(kp, vp, scale, causal=True, err_flag=err_flag, **dec_kw, **pre_kw)
+    if events is not None:
+        events[1].record(stream)
+    return slots, dec_out, pre_out
+
+
 def run_mode(pkv, torch, mode, args, prompt, output, arrival):
     dev = torch.device("cuda:0")
     hq, hkv, hd = 64, 8, 128
@@ -76,42 +124,19 @@ def run_mode(pkv, torch, mode, args, prompt, output, arrival):
     ws = pkv.decode_workspace(q_src[: args.max_running], hkv, max_blocks)
     scale = hd ** -0.5
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     now, steps, gpu_ms, t_wall = 0.0, 0, 0.0, time.perf_counter()
     while sched.num_done() < n:
         plan = sched.plan(now)
-        nd, nc = len(plan["dec_row"]), len(plan["chunk_row"])
-        if nd + nc == 0:
+        if len(plan["dec_row"]) + len(plan["chunk_row"]) == 0:
             if plan["next_arrival"] < 0:
                 raise RuntimeError("scheduler stalled with requests left")
             now = max(now, plan["next_arrival"])
             continue
         d_table.copy_(torch.from_numpy(sched.table))
-        rows = np.concatenate([plan["dec_row"], plan["chunk_row"]]).astype(np.int64)
-        lens = np.concatenate([np.ones(nd, np.int32), plan["chunk_len"]])
-        starts = np.concatenate([plan["dec_ctx"] - 1, plan["chunk_offset"]]).astype(np.int32)
-        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-        T = int(cu[-1])
-        t_rows = torch.from_numpy(rows).to(dev)
-        bt_all = d_table.index_select(0, t_rows)
-        cu_d, st_d = torch.from_numpy(cu).to(dev), torch.from_numpy(starts).to(dev)
-        dec_kw, pre_kw = {}, {}
-        if nd:
-            dec_kw = dict(dec_query=q_src[:nd], dec_block_tables=bt_all[:nd],
-                          context_lens=torch.from_numpy(plan["dec_ctx"]).to(dev), workspace=ws)
-        if nc:
-            ccu = np.concatenate([[0], np.cumsum(plan["chunk_len"])]).astype(np.int32)
-            pre_kw = dict(pre_query=q_src[nd:nd + int(ccu[-1])], cu_q_lens=torch.from_numpy(ccu).to(dev),
-                          chunk_offsets=torch.from_numpy(plan["chunk_offset"]).to(dev),
-                          pre_block_tables=bt_all[nd:], max_q_len=int(plan["chunk_len"].max()))
-        slots = torch.empty(T, dtype=torch.int32, device=dev)
-        e0.record(stream)
-        pkv.slot_mapping(bt_all, cu_d, st_d, int(lens.max()), nblk, out=slots)
-        pkv.cache_write(kv_src[:T], kv_src[:T], kp, vp, slots)
-        pkv.paged_attn_mixed(kp, vp, scale, causal=True, **dec_kw, **pre_kw)
-        e1.record(stream)
+        run_step(pkv, torch, kp, vp, d_table, plan, q_src, kv_src, kv_src, ws, scale, stream=stream, events=ev)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        ms = ev[0].elapsed_time(ev[1])
         gpu_ms += ms
         now += ms * 1e3  # microseconds of virtual time
         sched.complete(now)

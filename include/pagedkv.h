@@ -85,6 +85,10 @@ typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1, PKV_DTYPE_FP8_E4M3 = 2 } p
 #define PKV_FLAG_BAD_BLOCK 1   /* a block-table entry the call had to read is outside [0, num_blocks) */
 #define PKV_FLAG_BAD_SLOT 2    /* a slot is >= num_blocks * 16 */
 #define PKV_FLAG_BAD_LENGTH 4  /* a context / chunk end exceeds max_blocks_per_seq * 16, or is negative */
+#define PKV_FLAG_SYNC_TIMEOUT 8 /* pkv_paged_attn_mixed / the shared-prefix decode: a wave of a decode
+                                   worker gave up a bounded wait on its sibling waves (about 2^28
+                                   cycles); that call's outputs are unspecified.  Never set by a
+                                   correct run; with err_flag == NULL the event is not reported. */
 
 /* Static description of a status code. */
 const char* pkv_status_string(pkv_status status);

@@ -29,7 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, NO_SPACE = 0, 1, 2, 3, 4, 5
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
-FLAG_BAD_BLOCK, FLAG_BAD_SLOT, FLAG_BAD_LENGTH = 1, 2, 4
+FLAG_BAD_BLOCK, FLAG_BAD_SLOT, FLAG_BAD_LENGTH, FLAG_SYNC_TIMEOUT = 1, 2, 4, 8
 BLOCK_SIZE = 16
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstddef>
 
+#include "addressing.hpp"
 #include "pagedkv.h"
 
 namespace pkv {
@@ -41,8 +42,9 @@ __device__ __forceinline__ int64_t pool_slot_byte(int64_t slot, int w, int head_
 }
 
 // Byte offset of (block, in-block offset c_bytes) in a pool whose blocks are blk_bytes long.  With
-// NARROW (the whole pool below 4 GiB and fewer than 2^24 blocks) the offset is a 32-bit value built
-// with a 24-bit multiply, which lets the load use a scalar base plus a 32-bit vector offset.
+// NARROW (pkv_host::narrow_addressing: block ids and block bytes below 2^24, the whole pool below
+// 4 GiB) the offset is a 32-bit value built with a 24-bit multiply, which lets the load use a
+// scalar base plus a 32-bit vector offset.
 template <bool NARROW>
 __device__ __forceinline__ const char* pool_at(const void* pool, int block, uint32_t blk_bytes, uint32_t c_bytes) {
   if constexpr (NARROW) {
@@ -98,19 +100,26 @@ struct WgSync {
 // Barrier of one 256-thread half (waves 4h .. 4h + 3) of a 512-thread workgroup, so that the two
 // halves can run separate programs: each wave adds one arrival to the half's LDS counter (zero at
 // start) and waits until all four waves of the current round have arrived.  The wait is bounded
-// (about 2^22 polls of 64 cycles) so that a wave can never spin forever.
+// (about 2^22 polls of 64 cycles, far beyond any real wait) so that a wave can never spin forever;
+// a wave that gives up ORs PKV_FLAG_SYNC_TIMEOUT into err_flag (when the call has one): the
+// half's staging data can then be corrupt and the outputs are unspecified.
 struct HalfSync {
   int* cnt;
   int target;
+  int32_t* err_flag;
   __device__ void operator()() {
     target += 4;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    bool arrived = false;
     for (int spins = 0; spins < (1 << 22); ++spins) {
-      if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= target)
+      if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= target) {
+        arrived = true;
         break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (!arrived && err_flag != nullptr && (threadIdx.x & 63) == 0) atomicOr(err_flag, PKV_FLAG_SYNC_TIMEOUT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 };

@@ -457,9 +457,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* query, const 
     const int64_t resident = static_cast<int64_t>(pkv_host::cu_count()) * (head_dim <= 128 ? 2 : 1);
     const unsigned nwg = static_cast<unsigned>(max_items < resident ? max_items : resident);
     const int queues = nwg % kMaxQueues == 0 ? kMaxQueues : (nwg % 8 == 0 ? 8 : 1);
-    const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) <
-                            (1ull << 32) &&
-                        num_blocks < (1 << 24);
+    const bool narrow = pkv_host::narrow_addressing(num_blocks, num_kv_heads, head_dim, kv8 ? 1 : 2);
     launch_plan(err_flag != nullptr, context_lens, num_seqs, max_blocks_per_seq, S, pieces, plan,
                 static_cast<int>(nwg), queues, err_flag, st);
     if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
@@ -612,9 +610,7 @@ pkv_status decode_prefix_impl(void* out, pkv_dtype out_dtype, const void* query,
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool check = err_flag != nullptr;
-  const bool narrow =
-      static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) < (1ull << 32) &&
-      num_blocks < (1 << 24);
+  const bool narrow = pkv_host::narrow_addressing(num_blocks, num_kv_heads, head_dim, kv8 ? 1 : 2);
 
   // Prefix pass: rows (member, query head) of each KV head, key splits of the prefix.
   const int q_tiles = static_cast<int>((static_cast<int64_t>(num_members) * group + kPreTile - 1) / kPreTile);

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kPreThreads) void mixed_step_kernel(DecArgs da, con
     int* tail = reinterpret_cast<int*>(smem + 2 * M::DEC);  // [counter, fetched0, fetched1, pad] per half
     if ((threadIdx.x & 255) == 0) tail[4 * half] = 0;
     __syncthreads();  // both halves pass this once, before they go separate ways
-    HalfSync sync{tail + 4 * half, 0};
+    HalfSync sync{tail + 4 * half, 0, da.err_flag};
     decode_worker<HD, CHECK, NARROW, KV8>(da, pieces, plan, queues, half * dec_wgs + b, 2 * dec_wgs,
                                           smem + half * M::DEC, tail + 4 * half + 1, sync);
   } else {
@@ -121,9 +121,7 @@ extern "C" pkv_status pkv_paged_attn_mixed(
   const float vs = kv8 ? v_scale : 1.f;
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) <
-                          (1ull << 32) &&
-                      num_blocks < (1 << 24);
+  const bool narrow = pkv_host::narrow_addressing(num_blocks, num_kv_heads, head_dim, kv8 ? 1 : 2);
 
   // Decode part: the same plan, workspace layout and split size as pkv_paged_attn_decode.
   int dec_wgs = 0, queues = 1, S = 0, max_splits = 1;

@@ -6,16 +6,17 @@
 // the chunked result equals one-pass causal prefill.  Non-causal rows see the whole chunk end.
 //
 // Design (gfx950, wave64):
-//   * 1-D grid of (sequence, KV head, query head in group, 128-row query tile) work items; the
-//     workgroup id is remapped so that each XCD (workgroups are dealt round-robin over the 8 XCDs)
+//   * a work item is 256 query rows of one query head (eight waves of 32 rows) and one key split;
+//     the 1-D grid is remapped so that each XCD (workgroups are dealt round-robin over the 8 XCDs)
 //     gets a contiguous run of items, i.e. the query heads of one KV head, which then share that
 //     KV head's K/V stream in the XCD's L2.
-//   * 8 waves in two groups of four; each wave owns 32 query rows, and the two groups split the
-//     key range (even and odd key tiles), so every SIMD runs two independent waves whose MFMA and
-//     softmax work overlap.  The groups' (o, m, l) states are merged in LDS at the end.
+//   * when there are fewer row tiles than compute units, a row tile's key range is cut into up to
+//     eight splits of whole tile pairs, one workgroup each; every split writes its (o, m, l) partial
+//     to the workspace and prefill_merge_kernel combines them in split order after the launch.
 //   * key tiles (64 positions = 4 blocks; 32 for head_dim 256) are gathered through the block
-//     table by all 512 threads, a pair at a time, into double-buffered LDS; the next pair's loads
-//     are in flight while the current pair is computed, with one barrier per pair.
+//     table by all 512 threads, a pair at a time, into double-buffered LDS; all eight waves compute
+//     on both tiles of a pair; the next pair's loads are in flight while the current pair is
+//     computed, with one barrier per pair.  Block ids are staged in an LDS window.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q rows in registers);
 //     the accumulator layout gives each lane 16 keys of one query.  Only tiles crossing the causal
 //     diagonal or the key end are masked.  The reference max the exponentials subtract trails the
@@ -153,9 +154,7 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
   const float vs = kv8 ? v_scale : 1.f;
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool narrow = static_cast<uint64_t>(num_blocks) * kBlockSize * num_kv_heads * head_dim * (kv8 ? 1 : 2) <
-                          (1ull << 32) &&
-                      num_blocks < (1 << 24);
+  const bool narrow = pkv_host::narrow_addressing(num_blocks, num_kv_heads, head_dim, kv8 ? 1 : 2);
   const PreArgs pa{static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
                    max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks, causal != 0,
                    scale_log2, vs, out, ob, err_flag, ksplit,

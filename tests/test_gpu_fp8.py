@@ -3,7 +3,9 @@
 Bars: the quantising write is bit-exact (whole code pools compared byte for byte against
 oracle/fp8.py); decode and prefill over FP8 pools are compared with exact attention over the
 dequantised pools (value(code) * scale) at the bf16 tolerance (max-abs <= 1e-2, mean-abs <= 1e-3),
-and a one-key decode returns the dequantised V rows exactly.  Pools are built by quantising the
+and a one-key decode returns the dequantised V rows exactly.  Every test runs in both call modes
+(checked kernels with an err_flag, and the release kernels production callers run, err_flag NULL).
+Pools are built by quantising the
 bf16 pools of the ordinary generators (dead slots hold NaN there, so they become NaN codes here and
 any stray read shows up); scales: K 0.0123 (not a power of two, some inputs saturate), V 2^-5.
 """
@@ -15,6 +17,7 @@ import pytest
 import oracle
 from oracle import fp8 as ofp8
 import workloads as wl
+from gpu_common import MODES, flag, fp8_decode_reference, fp8_prefill_reference, mixed_step_case, new_err
 
 torch = pytest.importorskip("torch")
 
@@ -96,7 +99,8 @@ def close(got, ref, what):
     return d.max(), d.mean()
 
 
-def test_quantising_write_bit_exact_special_values(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_quantising_write_bit_exact_special_values(pkv, dev, mode):
     """Ties, subnormals, saturation, signed zeros, infinities and NaN, from bf16 and fp32 rows,
     with strided input rows and skipped (negative) slots."""
     _say("case fp8 write: special values, bf16 and fp32 inputs")
@@ -121,15 +125,16 @@ def test_quantising_write_bit_exact_special_values(pkv, dev):
             kp0 = rng.integers(0, 256, (nblk, hkv, 16, hd), dtype=np.uint8)
             vp0 = rng.integers(0, 256, (nblk, hkv, 16, hd), dtype=np.uint8)
             kp, vp = to_dev(kp0, dev).view(torch.float8_e4m3fn), to_dev(vp0, dev).view(torch.float8_e4m3fn)
-            err = torch.zeros(1, dtype=torch.int32, device=dev)
+            err = new_err(dev, mode)
             pkv.cache_write_fp8(xin, xin, kp, vp, to_dev(slots, dev), scale, V_SCALE, err_flag=err)
             rk, rv = ofp8.cache_write_fp8(kp0, vp0, xf, xf, slots, scale, V_SCALE)
             assert codes_of(kp).tobytes() == rk.tobytes(), f"K codes differ ({in_dt}, scale {scale})"
             assert codes_of(vp).tobytes() == rv.tobytes(), f"V codes differ ({in_dt}, scale {scale})"
-            assert int(err.item()) == 0
+            assert flag(err) == 0
 
 
-def test_one_key_decode_returns_dequantised_values(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_one_key_decode_returns_dequantised_values(pkv, dev, mode):
     """With one cached position the softmax weight is exactly 1, so the output is the dequantised V
     row: every finite code times the power-of-two V scale, exactly."""
     _say("case fp8 decode: one-key sequences over every code")
@@ -145,7 +150,8 @@ def test_one_key_decode_returns_dequantised_values(pkv, dev):
     q = to_dev(wl.f32_to_bf16_bits(rng.standard_normal((n_seq, hq, hd)).astype(np.float32)), dev, True)
     bt = to_dev(np.arange(n_seq, dtype=np.int32)[:, None], dev)
     ctx = to_dev(np.ones(n_seq, np.int32), dev)
-    out = pkv.paged_attn_decode_fp8(q, kp, vp, bt, ctx, hd ** -0.5, K_SCALE, V_SCALE).cpu().numpy()
+    out = pkv.paged_attn_decode_fp8(q, kp, vp, bt, ctx, hd ** -0.5, K_SCALE, V_SCALE,
+                                    err_flag=new_err(dev, mode)).cpu().numpy()
     want = ofp8.dequantize(vp0[:, :, 0], V_SCALE)  # [n_seq, hkv, hd]
     for h in range(hq):
         assert np.array_equal(out[:, h].astype(np.float64), want[:, oracle.kv_head_of(h, hq, hkv)])
@@ -161,11 +167,12 @@ FP8_DECODE = [
 
 
 @pytest.mark.parametrize("hq,hkv,hd,max_ctx,min_ctx", FP8_DECODE)
-def test_fp8_decode_matches_oracle(pkv, dev, hq, hkv, hd, max_ctx, min_ctx):
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_decode_matches_oracle(pkv, dev, mode, hq, hkv, hd, max_ctx, min_ctx):
     _say(f"case fp8 decode: hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx}")
     c = wl.random_case(5 * hq + hd + max_ctx, kind="decode", dtype="bf16", num_seqs=9, num_q_heads=hq,
                        num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, min_ctx=min_ctx, poison=True)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     kp, vp, rk, rv = quantised_pools(pkv, c, dev, err)
     rk, rv = write_new(pkv, c, dev, kp, vp, rk, rv, err)
     ref = oracle.decode(c.query, ofp8.dequantize(rk, K_SCALE), ofp8.dequantize(rv, V_SCALE), c.block_tables,
@@ -176,13 +183,14 @@ def test_fp8_decode_matches_oracle(pkv, dev, hq, hkv, hd, max_ctx, min_ctx):
                                         err_flag=err)
         mx, mean = close(out.cpu().numpy(), ref, f"fp8 decode split={split}")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_fp8_chunked_prefill_equals_one_pass(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_chunked_prefill_equals_one_pass(pkv, dev, mode):
     _say("case fp8 chunked prefill: 1000 tokens in chunks 256/256/256/232, 8 heads x 64")
     c = wl.chunked_prefill(poison=True)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     kp, vp, rk, rv = quantised_pools(pkv, c, dev, err)
     bt = to_dev(c.block_tables, dev)
     outs = []
@@ -204,7 +212,7 @@ def test_fp8_chunked_prefill_equals_one_pass(pkv, dev):
                                "bf16", kv_dtype="f64")
     mx, mean = close(np.concatenate(outs), one, "fp8 chunked vs one pass")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 FP8_PREFILL = [
@@ -217,12 +225,13 @@ FP8_PREFILL = [
 
 
 @pytest.mark.parametrize("hq,hkv,hd,max_ctx,q_len_max,causal", FP8_PREFILL)
-def test_fp8_prefill_matches_oracle(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, causal):
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_prefill_matches_oracle(pkv, dev, mode, hq, hkv, hd, max_ctx, q_len_max, causal):
     _say(f"case fp8 prefill: hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx} L<={q_len_max} causal={causal}")
     c = wl.random_case(7 * hq + hd + max_ctx + q_len_max, kind="prefill", dtype="bf16", num_seqs=4,
                        num_q_heads=hq, num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, q_len_max=q_len_max,
                        causal=causal, poison=True)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     kp, vp, rk, rv = quantised_pools(pkv, c, dev, err)
     rk, rv = write_new(pkv, c, dev, kp, vp, rk, rv, err)
     maxl = int(np.diff(c.cu_q_lens).max())
@@ -234,29 +243,18 @@ def test_fp8_prefill_matches_oracle(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, c
                                kv_dtype="f64")
     mx, mean = close(out.cpu().numpy(), ref, "fp8 prefill")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def _compact(codes, tables, lens, seqs):
-    """The blocks the listed sequences read, packed into a small pool, and their tables rewritten
-    to it (so the oracle dequantises only what it needs)."""
-    nb = [-(-int(lens[s]) // 16) for s in seqs]
-    ids = np.unique(np.concatenate([tables[s, :n] for s, n in zip(seqs, nb)]))
-    where = {int(b): i for i, b in enumerate(ids)}
-    t = np.full((len(seqs), max(nb)), wl.UNUSED_BLOCK_ID, np.int32)
-    for r, (s, n) in enumerate(zip(seqs, nb)):
-        t[r, :n] = [where[int(b)] for b in tables[s, :n]]
-    return codes[ids], t
-
-
-def test_fp8_mixed_step_full_size(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_mixed_step_full_size(pkv, dev, mode):
     """The mixed-step workload at full size over E4M3 pools, in the configuration the benchmark
     runs (library-chosen split size, one workspace): the whole pools quantised by the library's
     write and compared byte for byte, then the decode of all 127 sequences and the 512-row chunk;
-    sampled sequences and rows against the oracle over the dequantised pools."""
+    every sequence and every row against the oracle over the dequantised pools."""
     _say("case fp8 mixed step: 127 decode sequences + 512-row chunk at 16,384, 64/8 x 128, E4M3 pools")
-    dec, pre = wl.mixed_step(poison=True)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dec, pre, _, _, _ = mixed_step_case()
+    err = new_err(dev, mode)
     nblk, hkv, b, hd = pre.key_pool.shape
     kp = torch.empty((nblk, hkv, b, hd), dtype=torch.float8_e4m3fn, device=dev)
     vp = torch.empty_like(kp)
@@ -273,21 +271,10 @@ def test_fp8_mixed_step_full_size(pkv, dev):
                                              int(np.diff(pre.cu_q_lens).max()), pre.scale, K_SCALE, V_SCALE,
                                              causal=True, err_flag=err)
     d_out, p_out = d_out.cpu().numpy(), p_out.cpu().numpy()
-    assert int(err.item()) == 0
-    assert np.isfinite(d_out).all() and np.isfinite(p_out).all()
-    ctx = dec.context_lens
-    seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 1, 63, 126})
-    kc, t = _compact(rk, dec.block_tables, ctx, seqs)
-    vc, _ = _compact(rv, dec.block_tables, ctx, seqs)
-    ref = oracle.decode(dec.query[seqs], ofp8.dequantize(kc, K_SCALE), ofp8.dequantize(vc, V_SCALE), t, ctx[seqs],
-                        dec.scale, "bf16", kv_dtype="f64")
-    mx, mean = close(d_out[seqs], ref, "fp8 mixed decode (sampled sequences)")
-    _say(f"  decode ({len(seqs)} sequences) max-abs {mx:.2e} mean-abs {mean:.2e}")
-    plen = pre.chunk_offsets + np.diff(pre.cu_q_lens)
-    kc, t = _compact(rk, pre.block_tables, plen, [0])
-    vc, _ = _compact(rv, pre.block_tables, plen, [0])
-    rows = np.unique(np.concatenate([np.arange(0, 512, 13), np.arange(500, 512)]))
-    ref = oracle.prefill_chunk(pre.query, pre.cu_q_lens, pre.chunk_offsets, ofp8.dequantize(kc, K_SCALE),
-                               ofp8.dequantize(vc, V_SCALE), t, pre.scale, "bf16", rows=rows, kv_dtype="f64")
-    mx, mean = close(p_out[rows], ref[rows], "fp8 mixed prefill (sampled rows)")
-    _say(f"  prefill ({len(rows)} rows) max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert flag(err) == 0
+    ref = fp8_decode_reference(dec, rk, rv, K_SCALE, V_SCALE)
+    mx, mean = close(d_out, ref, "fp8 mixed decode (all 127 sequences)")
+    _say(f"  decode (all {dec.num_seqs} sequences) max-abs {mx:.2e} mean-abs {mean:.2e}")
+    ref = fp8_prefill_reference(pre, rk, rv, K_SCALE, V_SCALE)
+    mx, mean = close(p_out, ref, "fp8 mixed prefill (all 512 rows)")
+    _say(f"  prefill (all {p_out.shape[0]} rows) max-abs {mx:.2e} mean-abs {mean:.2e}")

@@ -7,7 +7,8 @@ in a small pool (a table maps logical blocks to any physical ones, "ç¬¬2ç« :æŽ¨ç
 The cache write, the decode, the prefill chunk and the fused launch are compared that way, with
 bf16 pools (32 KiB blocks, ids from 132,072) and E4M3 pools (16 KiB blocks, ids from 263,144),
 and the outputs are also checked against the oracle.  Blocks outside the case are never touched,
-so the large pools are left uninitialised.
+so the large pools are left uninitialised.  Both call modes run (checked kernels with an err_flag,
+and the release kernels, err_flag NULL).
 """
 import sys
 
@@ -17,6 +18,7 @@ import pytest
 import oracle
 from oracle import fp8 as ofp8
 import workloads as wl
+from gpu_common import MODES, flag, new_err
 
 torch = pytest.importorskip("torch")
 
@@ -58,10 +60,10 @@ def shift_ids(bt, base):
     return out
 
 
-def run_all(pkv, dev, c, dq, kp, vp, bt, num_blocks, fp8):
+def run_all(pkv, dev, c, dq, kp, vp, bt, num_blocks, fp8, mode):
     """Cache write of the case's new tokens, then decode, prefill and the fused launch over the
     same pools and table; returns the outputs on the host."""
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     maxl = int(np.diff(c.new_cu_lens).max())
     d_bt = to_dev(bt, dev)
     slots = pkv.slot_mapping(d_bt, to_dev(c.new_cu_lens, dev), to_dev(c.new_start_pos, dev), maxl, num_blocks,
@@ -88,7 +90,7 @@ def run_all(pkv, dev, c, dq, kp, vp, bt, num_blocks, fp8):
                                   max_q_len=qmax, causal=True, k_scale=scales[0] if fp8 else 1.0,
                                   v_scale=scales[1] if fp8 else 1.0, err_flag=err)
     torch.cuda.synchronize()
-    assert int(err.item()) == 0, f"device checks flagged {int(err.item()):#x}"
+    assert flag(err) == 0, f"device checks flagged {flag(err):#x}"
     # The case's blocks in logical order (sequence by sequence), as raw bytes.
     used = torch.from_numpy(bt[bt != wl.UNUSED_BLOCK_ID].astype(np.int64)).to(dev)
     rows_k = kp.view(torch.uint8).index_select(0, used).cpu()
@@ -98,7 +100,8 @@ def run_all(pkv, dev, c, dq, kp, vp, bt, num_blocks, fp8):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
-def test_pools_past_4gib_bit_identical(pkv, fp8):
+@pytest.mark.parametrize("mode", MODES)
+def test_pools_past_4gib_bit_identical(pkv, mode, fp8):
     dev = torch.device("cuda:0")
     elem = 1 if fp8 else 2
     blk_bytes = 16 * HKV * HD * elem
@@ -132,8 +135,8 @@ def test_pools_past_4gib_bit_identical(pkv, fp8):
     kb.view(torch.uint8).index_copy_(0, ids, ks.view(torch.uint8))
     vb.view(torch.uint8).index_copy_(0, ids, vs.view(torch.uint8))
     del k16, v16
-    small = run_all(pkv, dev, c, dq, ks, vs, c.block_tables, c.num_blocks, fp8)
-    big = run_all(pkv, dev, c, dq, kb, vb, shift_ids(c.block_tables, base), nbig, fp8)
+    small = run_all(pkv, dev, c, dq, ks, vs, c.block_tables, c.num_blocks, fp8, mode)
+    big = run_all(pkv, dev, c, dq, kb, vb, shift_ids(c.block_tables, base), nbig, fp8, mode)
     names = ["decode", "prefill", "fused decode", "fused prefill"]
     for name, a, b in zip(names, small[:4], big[:4]):
         assert a.tobytes() == b.tobytes(), f"{name} differs between the small and the large pool"

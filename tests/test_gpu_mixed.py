@@ -4,7 +4,8 @@ The fused call runs the decode and prefill device code of the separate calls in 
 bar is bit-identity with pkv_paged_attn_decode + pkv_paged_attn_prefill_chunk on the same inputs
 (bf16 and FP8 pools), plus the usual oracle tolerance (max-abs <= 1e-2, mean-abs <= 1e-3) on the
 fused outputs.  Cases: the 127-sequence mixed step with its 512-row chunk, small random batches
-with both parts over one pool, and each part alone.
+with both parts over one pool, and each part alone.  Every test runs in both call modes (checked
+kernels with an err_flag, and the release kernels production callers run, err_flag NULL).
 """
 import sys
 
@@ -14,6 +15,7 @@ import pytest
 import oracle
 from oracle import fp8 as ofp8
 import workloads as wl
+from gpu_common import MODES, flag, mixed_step_case, mixed_step_reference, new_err
 
 torch = pytest.importorskip("torch")
 
@@ -49,7 +51,7 @@ def close(got, ref, what):
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     d = np.abs(got - ref)
     assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS, f"{what}: max-abs {d.max():.3e} mean-abs {d.mean():.3e}"
-    return d.max(), d.mean()
+    return float(d.max()), float(d.mean())
 
 
 def run_both(pkv, kp, vp, scale, dq, dbt, dctx, pq, cu, offs, pbt, maxl, causal=True, fp8=None, err=None):
@@ -74,16 +76,18 @@ def run_both(pkv, kp, vp, scale, dq, dbt, dctx, pq, cu, offs, pbt, maxl, causal=
     return host(sep_d), host(sep_p), host(fd), host(fp)
 
 
-def test_fused_mixed_step_bit_identical(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_fused_mixed_step_bit_identical(pkv, dev, mode):
     """The mixed-step workload: 127 decode sequences (shared 63-block prefix) and a 512-row chunk at
     offset 16,384 of a 32,768-token prompt, after the chunk's cache write."""
     _say("case fused mixed step: 127 decode sequences + 512-row chunk, 64/8 x 128, bf16")
-    dec, pre = wl.mixed_step(poison=True)
+    dec, pre, ref_slots, _, _ = mixed_step_case()
     kp, vp = to_dev(dec.key_pool, dev, True), to_dev(dec.value_pool, dev, True)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     T = pre.num_new_tokens
     slots = pkv.slot_mapping(to_dev(pre.block_tables, dev), to_dev(pre.new_cu_lens, dev), to_dev(pre.new_start_pos, dev),
                              T, pre.num_blocks, err_flag=err, total=T)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
     pkv.cache_write(to_dev(pre.key_new, dev, True), to_dev(pre.value_new, dev, True), kp, vp, slots, err_flag=err)
     args = (to_dev(dec.query, dev, True), to_dev(dec.block_tables, dev), to_dev(dec.context_lens, dev),
             to_dev(pre.query, dev, True), to_dev(pre.cu_q_lens, dev), to_dev(pre.chunk_offsets, dev),
@@ -91,17 +95,13 @@ def test_fused_mixed_step_bit_identical(pkv, dev):
     sd, sp, fd, fp = run_both(pkv, kp, vp, dec.scale, *args, err=err)
     assert fd.tobytes() == sd.tobytes(), "fused decode differs from the decode call"
     assert fp.tobytes() == sp.tobytes(), "fused prefill differs from the prefill call"
-    assert int(err.item()) == 0
-    # Oracle spot checks of the fused outputs (the separate calls are checked in full elsewhere).
-    rk, rv = oracle.cache_write(dec.key_pool, dec.value_pool, pre.key_new, pre.value_new,
-                                oracle.slot_mapping(pre.block_tables, pre.new_cu_lens, pre.new_start_pos, 16))
-    pick = [0, 5, 63, 126]
-    ref_d = oracle.decode(dec.query[pick], rk, rv, dec.block_tables[pick], dec.context_lens[pick], dec.scale, "bf16")
-    close(fd[pick], ref_d, "fused decode vs oracle")
-    rows = [0, 200, 511]
-    ref_p = oracle.prefill_chunk(pre.query, pre.cu_q_lens, pre.chunk_offsets, rk, rv, pre.block_tables, pre.scale,
-                                 "bf16", rows=rows)
-    close(fp[rows], ref_p[rows], "fused prefill vs oracle")
+    assert flag(err) == 0
+    # The fused outputs against the oracle: every decode sequence and every chunk row.
+    ref_d, ref_p = mixed_step_reference()
+    mx, mean = close(fd, ref_d, "fused decode vs oracle (all 127 sequences)")
+    _say(f"  decode max-abs {mx:.2e} mean-abs {mean:.2e}")
+    mx, mean = close(fp, ref_p, "fused prefill vs oracle (all 512 rows)")
+    _say(f"  prefill max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
 MIXED_CASES = [
@@ -114,13 +114,14 @@ MIXED_CASES = [
 
 
 @pytest.mark.parametrize("hq,hkv,hd,max_ctx,q_len_max,fp8", MIXED_CASES)
-def test_fused_random_batches(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, fp8):
+@pytest.mark.parametrize("mode", MODES)
+def test_fused_random_batches(pkv, dev, mode, hq, hkv, hd, max_ctx, q_len_max, fp8):
     """Both parts over one pool: the prefill sequences' chunks, and one decode token per sequence
     at the end of each sequence's cached range; also each part alone."""
     _say(f"case fused random: hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx} L<={q_len_max} fp8={fp8}")
     c = wl.random_case(hq + 11 * hd + max_ctx + q_len_max, kind="prefill", dtype="bf16", num_seqs=6, num_q_heads=hq,
                        num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, q_len_max=q_len_max, causal=True, poison=True)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     kp, vp = to_dev(c.key_pool, dev, True), to_dev(c.value_pool, dev, True)
     maxl = int(np.diff(c.cu_q_lens).max())
     slots = pkv.slot_mapping(to_dev(c.block_tables, dev), to_dev(c.new_cu_lens, dev), to_dev(c.new_start_pos, dev),
@@ -167,4 +168,4 @@ def test_fused_random_batches(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, fp8):
     _, _, fd, fp = run_both(pkv, kp, vp, c.scale, dq, dbt, dctx, pq, cu, offs, pbt, maxl, fp8=scales, err=err)
     close(fd, ref_d, "fused decode vs oracle")
     close(fp, ref_p, "fused prefill vs oracle")
-    assert int(err.item()) == 0
+    assert flag(err) == 0

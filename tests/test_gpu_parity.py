@@ -6,9 +6,13 @@ Every call goes through the C ABI (via the ctypes binding).  Bars:
     against the oracle on N(0,1) inputs;
   * attention from fp32 inputs: max-abs <= 1e-4 (fp32 accumulation over at most a few thousand
     terms plus the hardware exp2's ~1 ulp error stay far below this);
-  * physical-id permutation and repeated runs: bit-identical outputs; split size: within 5e-6.
-Parity runs in checked mode (err_flag given) with NaN-poisoned dead slots and out-of-range ids
-in unused block-table entries, so a stray read shows up as a NaN or a flag.
+  * physical-id permutation and repeated runs: bit-identical outputs;
+  * split sizes: each split size against the oracle at the tolerance above, and the spread between
+    split sizes bounded by SPLIT_SPREAD (the bf16 rounding of the softmax weights, see the test).
+Every test runs in both call modes (gpu_common.MODES): checked (err_flag given: the kernels check
+each id and slot) and release (err_flag NULL: the kernel instances bench.py and production callers
+run, including the prefill's unmasked fast gather).  Inputs carry NaN-poisoned dead slots and
+out-of-range ids in unused block-table entries, so a stray read shows up as a NaN or a flag.
 """
 import math
 import sys
@@ -18,6 +22,7 @@ import pytest
 
 import oracle
 import workloads as wl
+from gpu_common import MODES, flag, mixed_step_case, mixed_step_reference, new_err
 
 torch = pytest.importorskip("torch")
 
@@ -25,6 +30,7 @@ pytestmark = pytest.mark.gpu
 
 BF16_MAX_ABS, BF16_MEAN_ABS = 1e-2, 1e-3
 F32_MAX_ABS = 1e-4
+SPLIT_SPREAD = 1.5e-3
 
 
 def _say(msg):
@@ -56,10 +62,6 @@ def to_host_storage(t, dtype):
     if dtype == "bf16":
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
-
-
-def new_err(dev):
-    return torch.zeros(1, dtype=torch.int32, device=dev)
 
 
 def assert_close(got, ref, dtype, what):
@@ -118,11 +120,12 @@ def oracle_pools_after_write(c, slots):
 # ------------------------------------------------------------------------------------------
 
 
-def test_tiny_write_and_gather_bit_exact(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_write_and_gather_bit_exact(pkv, dev, mode):
     _say("case tiny_decode: slot mapping + cache write + paged gather (fp32, 295 tokens)")
     c = wl.tiny_decode(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     assert to_host_storage(d.kp, c.dtype).tobytes() == rk.tobytes()
@@ -136,28 +139,30 @@ def test_tiny_write_and_gather_bit_exact(pkv, dev):
     assert to_host_storage(vg, c.dtype).tobytes() == exp_v.tobytes()
     # Gathered rows are the generator's contiguous tokens again.
     assert exp_k.tobytes() == c.key_new.tobytes()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_long_decode_write_bit_exact(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_long_decode_write_bit_exact(pkv, dev, mode):
     _say("case long_decode: write of 58 x 16 tokens into the last blocks (bf16, 4x256)")
     c = wl.long_decode(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     assert to_host_storage(d.kp, c.dtype).tobytes() == rk.tobytes()
     assert to_host_storage(d.vp, c.dtype).tobytes() == rv.tobytes()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_write_skips_negative_slots_and_strided_rows(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_write_skips_negative_slots_and_strided_rows(pkv, dev, mode):
     _say("case write: negative slots, strided key/value rows, fp32 and bf16")
     for dtype in ("f32", "bf16"):
         c = wl.random_case(3, kind="prefill", dtype=dtype, num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=64,
                            max_ctx=200, q_len_max=40, poison=True)
         d = Dev(c, dev)
-        err = new_err(dev)
+        err = new_err(dev, mode)
         slots = oracle.slot_mapping(c.block_tables, c.new_cu_lens, c.new_start_pos, 16)
         slots[::3] = -1
         # Rows taken from a wider buffer: token stride = 2 rows.
@@ -172,14 +177,15 @@ def test_write_skips_negative_slots_and_strided_rows(pkv, dev):
         rk, rv = oracle.cache_write(c.key_pool, c.value_pool, c.key_new, c.value_new, slots)
         assert to_host_storage(d.kp, dtype).tobytes() == rk.tobytes()
         assert to_host_storage(d.vp, dtype).tobytes() == rv.tobytes()
-        assert int(err.item()) == 0
+        assert flag(err) == 0
 
 
-def test_gather_bit_exact_gqa_decode(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_gather_bit_exact_gqa_decode(pkv, dev, mode):
     _say("case gqa_decode: paged gather of all 128 sequences (bf16, 8x128)")
     c = wl.gqa_decode(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     cu = np.concatenate([[0], np.cumsum(c.context_lens)]).astype(np.int32)
     kg, vg = pkv.paged_gather(d.kp, d.vp, d.bt, d.ctx, to_dev(cu, dev), int(c.context_lens.max()), int(cu[-1]),
                               err_flag=err)
@@ -188,7 +194,7 @@ def test_gather_bit_exact_gqa_decode(pkv, dev):
         n = int(c.context_lens[s])
         assert kh[cu[s]:cu[s] + n].tobytes() == oracle.gather(c.key_pool, c.block_tables[s], n).tobytes()
         assert vh[cu[s]:cu[s] + n].tobytes() == oracle.gather(c.value_pool, c.block_tables[s], n).tobytes()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 # ------------------------------------------------------------------------------------------
@@ -201,67 +207,78 @@ def _decode(pkv, d, **kw):
     return pkv.paged_attn_decode(to_dev(c.query, d.dev, c.dtype), d.kp, d.vp, d.bt, d.ctx, c.scale, **kw)
 
 
-def test_tiny_decode_fp32(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_decode_fp32(pkv, dev, mode):
     _say("case tiny_decode: write + decode, fp32, 8 heads x 64, contexts 17/50/100/128")
     c = wl.tiny_decode(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, "f32")
     for split in (0, 128):
         out = _decode(pkv, d, err_flag=err, split_tokens=split)
         assert_close(out.cpu().numpy(), ref, "f32", f"tiny decode split={split}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_gqa_decode_full(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_gqa_decode_full(pkv, dev, mode):
     _say("case gqa_decode: 128 seqs, 64/8 heads x 128, lognormal contexts, bf16 (whole output)")
     c = wl.gqa_decode(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     out = _decode(pkv, d, err_flag=err)
     ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
     mx, mean = assert_close(out.cpu().numpy(), ref, "bf16", "gqa decode")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_long_decode_full(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_long_decode_full(pkv, dev, mode):
     _say("case long_decode: write 16 tokens/seq, then decode 58 x 4096, 16/4 heads x 256, bf16")
     c = wl.long_decode(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     out = _decode(pkv, d, err_flag=err)
     ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, "bf16")
     mx, mean = assert_close(out.cpu().numpy(), ref, "bf16", "long decode")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_decode_split_size_invariance_and_determinism(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_split_size_invariance_and_determinism(pkv, dev, mode):
     _say("case decode subset: split sizes 128..2048, repeated runs")
     c = wl.random_case(91, kind="decode", dtype="bf16", num_seqs=9, num_q_heads=16, num_kv_heads=2, head_dim=128,
                        max_ctx=2100, min_ctx=1, new_tokens=False, poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     outs = {s: _decode(pkv, d, err_flag=err, split_tokens=s).cpu().numpy() for s in (128, 256, 512, 1024, 2048)}
     ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
     base = outs[512]
+    spread = 0.0
     for s, o in outs.items():
         assert_close(o, ref, "bf16", f"split {s}")
-        # Each split rescales and rounds its probabilities to bf16 for the P.V product on its own
-        # running max, so split sizes agree to the bf16 rounding of P (2^-9 relative per weight),
-        # not to fp32 rounding.
-        assert np.max(np.abs(o - base)) <= 5e-3, f"split {s} vs 512"
+        spread = max(spread, float(np.max(np.abs(o - base))))
+    _say(f"  largest difference between split sizes: {spread:.2e}")
+    # Each split rounds its softmax weights to bf16 (relative error <= 2^-9, different for each
+    # split size because each runs against its own reference max), so split sizes agree to that
+    # rounding, not to fp32 rounding.  Modelling the roundings as independent, an output element
+    # moves by ~2^-9/sqrt(3) * sqrt(sum w^2 (v - out)^2) / sum w, which for these contexts
+    # (129..2100 keys, N(0,1) data) gives a few 1e-4 at the largest of the 18k elements; the
+    # measured largest difference is ~5e-4, and the bound leaves a factor of about 3 over it.
+    assert spread <= SPLIT_SPREAD, f"split sizes differ by {spread:.3e}"
     again = _decode(pkv, d, err_flag=err, split_tokens=512).cpu().numpy()
     assert again.tobytes() == base.tobytes()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_decode_block_permutation_bit_identical(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_block_permutation_bit_identical(pkv, dev, mode):
     _say("case decode permutation: same data under permuted physical block ids")
     c = wl.random_case(92, kind="decode", dtype="bf16", num_seqs=6, num_q_heads=8, num_kv_heads=1, head_dim=128,
                        max_ctx=700, min_ctx=1, new_tokens=False, poison=True)
@@ -275,13 +292,13 @@ def test_decode_block_permutation_bit_identical(pkv, dev):
     used = bt != wl.UNUSED_BLOCK_ID
     bt[used] = perm[bt[used]]
     d1 = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     o1 = _decode(pkv, d1, err_flag=err, split_tokens=256).cpu().numpy()
     c2 = wl.PagedCase(**{**c.__dict__, "key_pool": kp, "value_pool": vp, "block_tables": bt})
     d2 = Dev(c2, dev)
     o2 = _decode(pkv, d2, err_flag=err, split_tokens=256).cpu().numpy()
     assert o1.tobytes() == o2.tobytes()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 DECODE_SWEEP = [
@@ -299,23 +316,25 @@ DECODE_SWEEP = [
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,hd,max_ctx,min_ctx", DECODE_SWEEP)
-def test_decode_sweep(pkv, dev, dtype, hq, hkv, hd, max_ctx, min_ctx):
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_sweep(pkv, dev, mode, dtype, hq, hkv, hd, max_ctx, min_ctx):
     _say(f"case decode sweep: {dtype} hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx}")
     c = wl.random_case(hq * 7 + hd + max_ctx, kind="decode", dtype=dtype, num_seqs=7, num_q_heads=hq,
                        num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, min_ctx=min_ctx, poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, dtype)
     for split in (0, 128):
         out = _decode(pkv, d, err_flag=err, split_tokens=split)
         assert_close(out.cpu().numpy(), ref, dtype, f"decode sweep split={split}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 @pytest.mark.parametrize("ctx_list", [[0, 1, 15, 16, 17], [31, 32, 33, 127, 128], [129, 511, 512, 513, 1]])
-def test_decode_edge_contexts(pkv, dev, ctx_list):
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_edge_contexts(pkv, dev, mode, ctx_list):
     _say(f"case decode edges: contexts {ctx_list}")
     c = wl.random_case(77, kind="decode", dtype="bf16", num_seqs=len(ctx_list), num_q_heads=8, num_kv_heads=2,
                        head_dim=128, max_ctx=600, min_ctx=0, poison=True, new_tokens=False)
@@ -335,28 +354,29 @@ def test_decode_edge_contexts(pkv, dev, ctx_list):
     c2 = wl.PagedCase(**{**c.__dict__, "key_pool": kp, "value_pool": vp, "block_tables": bt, "context_lens": ctx,
                          "num_blocks": nblk})
     d = Dev(c2, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     ref = oracle.decode(c2.query, kp, vp, bt, ctx, c2.scale, "bf16")
     for split in (0, 128, 256):
         out = _decode(pkv, d, err_flag=err, split_tokens=split).cpu().numpy()
         assert_close(out, ref, "bf16", f"edge decode split={split}")
         assert (out[ctx == 0] == 0).all()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_decode_bf16_output(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_decode_bf16_output(pkv, dev, mode):
     _say("case decode bf16 output")
     c = wl.random_case(93, kind="decode", dtype="bf16", num_seqs=5, num_q_heads=16, num_kv_heads=2, head_dim=128,
                        max_ctx=1500, min_ctx=1, new_tokens=False, poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     out = _decode(pkv, d, err_flag=err, out_dtype=torch.bfloat16).float().cpu().numpy()
     ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale, "bf16")
     diff = np.abs(out - ref)
     # bf16 rounding of the result adds at most half an ulp (2^-9 relative).
     assert (diff <= BF16_MAX_ABS + np.abs(ref) * 2.0 ** -8).all()
     assert diff.mean() <= BF16_MEAN_ABS + np.mean(np.abs(ref)) * 2.0 ** -9
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 # ------------------------------------------------------------------------------------------
@@ -370,11 +390,12 @@ def _prefill(pkv, d, q, cu, offs, max_q_len, causal=True, **kw):
                                         d.vp, d.bt, max_q_len, c.scale, causal=causal, **kw)
 
 
-def test_chunked_prefill_equals_one_pass(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_chunked_prefill_equals_one_pass(pkv, dev, mode):
     _say("case chunked_prefill: 1000 tokens in chunks 256/256/256/232 vs one pass, 8 heads x 64, bf16")
     c = wl.chunked_prefill(poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     outs = []
     kp_ref, vp_ref = c.key_pool, c.value_pool
     for (s, e) in c.notes["chunks"]:
@@ -397,7 +418,7 @@ def test_chunked_prefill_equals_one_pass(pkv, dev):
                        err_flag=err).cpu().numpy()
     assert_close(gpu_one, one, "bf16", "one pass")
     assert np.max(np.abs(gpu_one - np.concatenate(outs))) <= 2 * BF16_MAX_ABS
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 PREFILL_SWEEP = [
@@ -412,13 +433,14 @@ PREFILL_SWEEP = [
 
 
 @pytest.mark.parametrize("hq,hkv,hd,max_ctx,q_len_max,causal", PREFILL_SWEEP)
-def test_prefill_sweep(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, causal):
+@pytest.mark.parametrize("mode", MODES)
+def test_prefill_sweep(pkv, dev, mode, hq, hkv, hd, max_ctx, q_len_max, causal):
     _say(f"case prefill sweep: hq={hq} hkv={hkv} hd={hd} ctx<={max_ctx} L<={q_len_max} causal={causal}")
     c = wl.random_case(hq + 3 * hd + max_ctx + q_len_max, kind="prefill", dtype="bf16", num_seqs=5, num_q_heads=hq,
                        num_kv_heads=hkv, head_dim=hd, max_ctx=max_ctx, q_len_max=q_len_max, causal=causal,
                        poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     maxl = int(np.diff(c.cu_q_lens).max())
@@ -426,39 +448,58 @@ def test_prefill_sweep(pkv, dev, hq, hkv, hd, max_ctx, q_len_max, causal):
     ref = oracle.prefill_chunk(c.query, c.cu_q_lens, c.chunk_offsets, rk, rv, c.block_tables, c.scale, "bf16",
                                causal=causal)
     assert_close(out, ref, "bf16", "prefill sweep")
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_mixed_step(pkv, dev):
-    _say("case mixed_step: write 512 -> decode 127 seqs (shared 63-block prefix) -> prefill 512 @ 16384")
-    dec, pre = wl.mixed_step(poison=True)
+def _mixed_step_outputs(pkv, dev, mode):
+    """The benchmark's step on the mixed workload: write the chunk's 512 tokens, decode the 127
+    sequences, attend the chunk; returns (decode output, chunk output, err flag, the pools)."""
+    dec, pre, ref_slots, _, _ = mixed_step_case()
     d = Dev(pre, dev)  # pools shared by both parts
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
-    rk, rv = oracle_pools_after_write(pre, slots)
+    assert np.array_equal(slots, ref_slots)
     dd = Dev.__new__(Dev)
     dd.c, dd.dev, dd.kp, dd.vp = dec, dev, d.kp, d.vp
     dd.bt, dd.ctx = to_dev(dec.block_tables, dev), to_dev(dec.context_lens, dev)
     out_dec = _decode(pkv, dd, err_flag=err).cpu().numpy()
     out_pre = _prefill(pkv, d, pre.query, pre.cu_q_lens, pre.chunk_offsets, 512, err_flag=err).cpu().numpy()
-    assert int(err.item()) == 0
-    ref_dec = oracle.decode(dec.query, rk, rv, dec.block_tables, dec.context_lens, dec.scale, "bf16")
-    mx, mean = assert_close(out_dec, ref_dec, "bf16", "mixed decode")
+    return out_dec, out_pre, err, d
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mixed_step(pkv, dev, mode):
+    _say(f"case mixed_step ({mode}): write 512 -> decode 127 seqs (shared 63-block prefix) -> prefill 512 @ 16384")
+    out_dec, out_pre, err, d = _mixed_step_outputs(pkv, dev, mode)
+    assert flag(err) == 0
+    _, pre, _, rk, rv = mixed_step_case()
+    assert to_host_storage(d.kp, "bf16").tobytes() == rk.tobytes()
+    assert to_host_storage(d.vp, "bf16").tobytes() == rv.tobytes()
+    ref_dec, ref_pre = mixed_step_reference()
+    mx, mean = assert_close(out_dec, ref_dec, "bf16", "mixed decode (all 127 sequences)")
     _say(f"  decode max-abs {mx:.2e} mean-abs {mean:.2e}")
-    rows = np.unique(np.concatenate([np.arange(0, 512, 5), np.arange(496, 512)]))
-    ref_pre = oracle.prefill_chunk(pre.query, pre.cu_q_lens, pre.chunk_offsets, rk, rv, pre.block_tables, pre.scale,
-                                   "bf16", rows=rows)
-    mx, mean = assert_close(out_pre[rows], ref_pre[rows], "bf16", "mixed prefill (sampled rows)")
-    _say(f"  prefill ({len(rows)} sampled rows) max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert np.isfinite(out_pre).all()
+    mx, mean = assert_close(out_pre, ref_pre, "bf16", "mixed prefill (all 512 rows)")
+    _say(f"  prefill (all 512 rows) max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
-def test_prefill_bf16_output_and_determinism(pkv, dev):
+def test_mixed_step_release_equals_checked(pkv, dev):
+    """The checked instances only add id and slot checks: on valid inputs both modes give the same
+    bits, so the oracle comparisons of either mode carry over to the other."""
+    _say("case mixed_step: release vs checked kernels, bit for bit")
+    a_dec, a_pre, err, _ = _mixed_step_outputs(pkv, dev, "checked")
+    b_dec, b_pre, _, _ = _mixed_step_outputs(pkv, dev, "release")
+    assert flag(err) == 0
+    assert a_dec.tobytes() == b_dec.tobytes(), "decode: release and checked kernels differ"
+    assert a_pre.tobytes() == b_pre.tobytes(), "prefill: release and checked kernels differ"
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_prefill_bf16_output_and_determinism(pkv, dev, mode):
     _say("case prefill bf16 output + repeat")
     c = wl.random_case(94, kind="prefill", dtype="bf16", num_seqs=3, num_q_heads=8, num_kv_heads=2, head_dim=128,
                        max_ctx=600, q_len_max=260, poison=True)
     d = Dev(c, dev)
-    err = new_err(dev)
+    err = new_err(dev, mode)
     slots = write_new_tokens(pkv, d, err)
     rk, rv = oracle_pools_after_write(c, slots)
     maxl = int(np.diff(c.cu_q_lens).max())
@@ -470,7 +511,7 @@ def test_prefill_bf16_output_and_determinism(pkv, dev):
     ref = oracle.prefill_chunk(c.query, c.cu_q_lens, c.chunk_offsets, rk, rv, c.block_tables, c.scale, "bf16")
     diff = np.abs(ob - ref)
     assert (diff <= BF16_MAX_ABS + np.abs(ref) * 2.0 ** -8).all()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
 # ------------------------------------------------------------------------------------------
@@ -485,7 +526,8 @@ def _bf16_bits(rng, shape):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def test_copy_blocks_bit_exact(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_copy_blocks_bit_exact(pkv, dev, mode):
     _say("case copy_blocks: 300 of 1,000 bf16 blocks (8 x 128) copied, whole pools compared")
     rng = np.random.default_rng(11)
     nblk, hkv, hd = 1000, 8, 128
@@ -495,22 +537,24 @@ def test_copy_blocks_bit_exact(pkv, dev):
     src, dst = perm[:300].copy(), perm[300:600].copy()
     src[:5] = dst[:5]  # src == dst: no-op
     d_k, d_v = to_dev(kp, dev, "bf16"), to_dev(vp, dev, "bf16")
-    err = new_err(dev)
+    err = new_err(dev, mode)
     pkv.copy_blocks(d_k, d_v, to_dev(src, dev), to_dev(dst, dev), err_flag=err)
     ek, ev = kp.copy(), vp.copy()
     ek[dst] = kp[src]
     ev[dst] = vp[src]
     assert np.array_equal(to_host_storage(d_k, "bf16"), ek)
     assert np.array_equal(to_host_storage(d_v, "bf16"), ev)
-    assert int(err.item()) == 0
-    # Checked mode: an out-of-range id is flagged and its pair skipped.
-    bad = torch.tensor([nblk + 3], dtype=torch.int32, device=dev)
-    pkv.copy_blocks(d_k, d_v, bad, to_dev(dst[:1], dev), err_flag=err)
-    assert int(err.item()) & pkv.FLAG_BAD_BLOCK
-    assert np.array_equal(to_host_storage(d_k, "bf16"), ek)
+    assert flag(err) == 0
+    if mode == "checked":
+        # An out-of-range id is flagged and its pair skipped (checked instances only).
+        bad = torch.tensor([nblk + 3], dtype=torch.int32, device=dev)
+        pkv.copy_blocks(d_k, d_v, bad, to_dev(dst[:1], dev), err_flag=err)
+        assert int(err.item()) & pkv.FLAG_BAD_BLOCK
+        assert np.array_equal(to_host_storage(d_k, "bf16"), ek)
 
 
-def test_block_manager_prefix_cache_and_copy_on_write_decode(pkv, dev):
+@pytest.mark.parametrize("mode", MODES)
+def test_block_manager_prefix_cache_and_copy_on_write_decode(pkv, dev, mode):
     """Sequences built by the block manager: a shared system prompt (prefix-cache hits skip the
     write of its full blocks), parallel samples forked from one request (their shared, partly
     filled last block is copied on the first write), and a request freed before a new prompt
@@ -523,7 +567,7 @@ def test_block_manager_prefix_cache_and_copy_on_write_decode(pkv, dev):
     bm = pkv.BlockManager(nblk, free_order=rng.permutation(nblk).astype(np.int32))
     kp = torch.full((nblk, hkv, 16, hd), float("nan"), dtype=torch.bfloat16, device=dev)
     vp = torch.full_like(kp, float("nan"))
-    err = new_err(dev)
+    err = new_err(dev, mode)
     sys_tok = rng.integers(0, 30000, 100)
     sys_k, sys_v = _bf16_bits(rng, (100, hkv, hd)), _bf16_bits(rng, (100, hkv, hd))
     seqs = []  # dict(row, ctx, tokens, k, v): k, v = the sequence's logical rows (bf16 bits)
@@ -587,4 +631,4 @@ def test_block_manager_prefix_cache_and_copy_on_write_decode(pkv, dev):
             ref[s, h] = oracle.softmax_attention(qf[s, h][None], K[:, g], V[:, g], scale, np.array([ctx[s]]))[0]
     mx, mean = assert_close(out.cpu().numpy(), ref, "bf16", "block-manager decode")
     _say(f"  {B} sequences, max-abs {mx:.2e} mean-abs {mean:.2e}")
-    assert int(err.item()) == 0
+    assert flag(err) == 0

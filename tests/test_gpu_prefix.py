@@ -9,7 +9,9 @@ step's 127 sequences (63 shared blocks; the members are the sequences that reach
 the 64-sequence batch behind a 256-block shared prompt, both at full size; random batches in
 which a subset shares a prefix, with a member that ends exactly at the prefix, members whose
 rest spans several splits, non-members with empty contexts, and group sizes 1 to 16; and the
-no-member call, which must equal the plain decode bit for bit.
+no-member call, which must equal the plain decode bit for bit.  Every test except the flag test
+runs in both call modes (checked kernels with an err_flag, and the release kernels production
+callers run, err_flag NULL).
 """
 import sys
 
@@ -18,6 +20,7 @@ import pytest
 
 import oracle
 import workloads as wl
+from gpu_common import MODES, flag, new_err
 
 torch = pytest.importorskip("torch")
 
@@ -51,7 +54,8 @@ def close(got, ref, what):
     return d.max(), d.mean()
 
 
-def test_mixed_step_decode_with_shared_prefix(pkv):
+@pytest.mark.parametrize("mode", MODES)
+def test_mixed_step_decode_with_shared_prefix(pkv, mode):
     dev = torch.device("cuda:0")
     dec, _ = wl.mixed_step(poison=True)
     P = 63
@@ -59,11 +63,11 @@ def test_mixed_step_decode_with_shared_prefix(pkv):
     _say(f"case prefix decode: mixed step, {len(members)} members of {dec.num_seqs} sharing {P} blocks")
     kp, vp = to_dev(dec.key_pool, dev, True), to_dev(dec.value_pool, dev, True)
     q, bt, ctx = to_dev(dec.query, dev, True), to_dev(dec.block_tables, dev), to_dev(dec.context_lens, dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     out = pkv.paged_attn_decode_prefix(q, kp, vp, bt, ctx, dec.scale, to_dev(members, dev), P, err_flag=err)
     plain = pkv.paged_attn_decode(q, kp, vp, bt, ctx, dec.scale, err_flag=err)
     torch.cuda.synchronize()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
     ref = oracle.decode(dec.query, dec.key_pool, dec.value_pool, dec.block_tables, dec.context_lens, dec.scale, "bf16")
     mx, mean = close(out.cpu().numpy(), ref, "prefix decode vs oracle")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
@@ -71,7 +75,8 @@ def test_mixed_step_decode_with_shared_prefix(pkv):
     assert float(d.max()) <= 5e-3, f"prefix decode vs plain decode: max {float(d.max()):.3e}"
 
 
-def test_shared_prefix_workload_full_size(pkv):
+@pytest.mark.parametrize("mode", MODES)
+def test_shared_prefix_workload_full_size(pkv, mode):
     """The 64-sequence, 256-shared-block decode batch timed by the benchmark, in its launch
     configuration, against the oracle on every sequence and against the plain decode."""
     dev = torch.device("cuda:0")
@@ -80,13 +85,13 @@ def test_shared_prefix_workload_full_size(pkv):
     _say(f"case prefix decode: shared-prefix workload, {dec.num_seqs} members, {P} blocks")
     kp, vp = to_dev(dec.key_pool, dev, True), to_dev(dec.value_pool, dev, True)
     q, bt, ctx = to_dev(dec.query, dev, True), to_dev(dec.block_tables, dev), to_dev(dec.context_lens, dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     ws = pkv.decode_prefix_workspace(q, dec.num_kv_heads, dec.max_blocks_per_seq)
     out = pkv.paged_attn_decode_prefix(q, kp, vp, bt, ctx, dec.scale, to_dev(dec.notes["members"], dev), P,
                                        workspace=ws, err_flag=err)
     plain = pkv.paged_attn_decode(q, kp, vp, bt, ctx, dec.scale, err_flag=err)
     torch.cuda.synchronize()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
     ref = oracle.decode(dec.query, dec.key_pool, dec.value_pool, dec.block_tables, dec.context_lens, dec.scale, "bf16")
     mx, mean = close(out.cpu().numpy(), ref, "prefix decode vs oracle")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
@@ -152,7 +157,8 @@ PREFIX_CASES = [
 
 
 @pytest.mark.parametrize("hq,hkv,hd,P,mctx,octx,split", PREFIX_CASES)
-def test_shared_prefix_random(pkv, hq, hkv, hd, P, mctx, octx, split):
+@pytest.mark.parametrize("mode", MODES)
+def test_shared_prefix_random(pkv, mode, hq, hkv, hd, P, mctx, octx, split):
     dev = torch.device("cuda:0")
     _say(f"case prefix decode: hq={hq} hkv={hkv} hd={hd} P={P} members={len(mctx)} others={len(octx)} "
          f"split={split}")
@@ -160,12 +166,12 @@ def test_shared_prefix_random(pkv, hq, hkv, hd, P, mctx, octx, split):
     q, kpool, vpool, bt, ctx, members = shared_prefix_case(hq * 7 + hd + P, hq, hkv, hd, P, n, mctx, octx)
     kp, vp = to_dev(kpool, dev, True), to_dev(vpool, dev, True)
     qd, btd, ctxd = to_dev(q, dev, True), to_dev(bt, dev), to_dev(ctx, dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     scale = hd ** -0.5
     out = pkv.paged_attn_decode_prefix(qd, kp, vp, btd, ctxd, scale, to_dev(members, dev), P, split_tokens=split,
                                        err_flag=err)
     torch.cuda.synchronize()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
     ref = oracle.decode(q, kpool, vpool, bt, ctx, scale, "bf16")
     mx, mean = close(out.cpu().numpy(), ref, "prefix decode vs oracle")
     _say(f"  max-abs {mx:.2e} mean-abs {mean:.2e}")
@@ -174,10 +180,11 @@ def test_shared_prefix_random(pkv, hq, hkv, hd, P, mctx, octx, split):
                                          out_dtype=torch.bfloat16, err_flag=err)
     d = (out16.float() - out).abs()
     assert float(d.max()) <= 2.0 ** -7 * max(1.0, float(out.abs().max()))
-    assert int(err.item()) == 0
+    assert flag(err) == 0
 
 
-def test_no_members_is_the_plain_decode(pkv):
+@pytest.mark.parametrize("mode", MODES)
+def test_no_members_is_the_plain_decode(pkv, mode):
     dev = torch.device("cuda:0")
     _say("case prefix decode: no members")
     c = wl.random_case(77, kind="decode", dtype="bf16", num_seqs=7, num_q_heads=16, num_kv_heads=4, head_dim=128,
@@ -185,10 +192,14 @@ def test_no_members_is_the_plain_decode(pkv):
     kp, vp = to_dev(c.key_pool, dev, True), to_dev(c.value_pool, dev, True)
     q, bt, ctx = to_dev(c.query, dev, True), to_dev(c.block_tables, dev), to_dev(c.context_lens, dev)
     none = torch.zeros(0, dtype=torch.int32, device=dev)
-    a = pkv.paged_attn_decode_prefix(q, kp, vp, bt, ctx, c.scale, none, 5)
-    b = pkv.paged_attn_decode(q, kp, vp, bt, ctx, c.scale)
+    err = new_err(dev, mode)
+    a = pkv.paged_attn_decode_prefix(q, kp, vp, bt, ctx, c.scale, none, 5, err_flag=err)
+    b = pkv.paged_attn_decode(q, kp, vp, bt, ctx, c.scale, err_flag=err)
     torch.cuda.synchronize()
+    assert flag(err) == 0
     assert torch.equal(a, b)
+    close(a.cpu().numpy(), oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, c.scale,
+                                         "bf16"), "decode vs oracle")
 
 
 def test_bad_member_index_is_flagged_and_skipped(pkv):
@@ -210,7 +221,8 @@ def test_bad_member_index_is_flagged_and_skipped(pkv):
 
 
 @pytest.mark.parametrize("hq,hkv,hd,P,mctx,octx,split", [PREFIX_CASES[0], PREFIX_CASES[2], PREFIX_CASES[3]])
-def test_shared_prefix_fp8_pools(pkv, hq, hkv, hd, P, mctx, octx, split):
+@pytest.mark.parametrize("mode", MODES)
+def test_shared_prefix_fp8_pools(pkv, mode, hq, hkv, hd, P, mctx, octx, split):
     """E4M3 pools (quantised by the library's own write): the shared-prefix decode against the oracle
     over the dequantised pools and against the plain FP8 decode."""
     from oracle import fp8 as ofp8
@@ -224,14 +236,14 @@ def test_shared_prefix_fp8_pools(pkv, hq, hkv, hd, P, mctx, octx, split):
     vp = torch.empty_like(kp)
     pkv.cache_write_fp8(to_dev(wl.slot_rows(kpool), dev, True), to_dev(wl.slot_rows(vpool), dev, True), kp, vp,
                         torch.arange(nblk * 16, dtype=torch.int32, device=dev), ks, vs)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    err = new_err(dev, mode)
     qd, btd, ctxd = to_dev(q, dev, True), to_dev(bt, dev), to_dev(ctx, dev)
     scale = hd ** -0.5
     out = pkv.paged_attn_decode_prefix_fp8(qd, kp, vp, btd, ctxd, scale, ks, vs, to_dev(members, dev), P,
                                            split_tokens=split, err_flag=err)
     plain = pkv.paged_attn_decode_fp8(qd, kp, vp, btd, ctxd, scale, ks, vs, split_tokens=split, err_flag=err)
     torch.cuda.synchronize()
-    assert int(err.item()) == 0
+    assert flag(err) == 0
     rk = ofp8.dequantize(ofp8.quantize_bf16_bits(kpool, ks), ks)
     rv = ofp8.dequantize(ofp8.quantize_bf16_bits(vpool, vs), vs)
     mx, mean = close(out.cpu().numpy(), oracle.decode(q, rk, rv, bt, ctx, scale, "bf16", kv_dtype="f64"),

@@ -98,6 +98,20 @@ def test_write_then_gather_round_trip_is_bit_exact(block_size, storage):
     assert flat[slots[1::2]].tobytes() == seq_k[1::2].reshape(len(slots[1::2]), -1).tobytes()
 
 
+def test_bf16_widening_matches_torch_over_every_pattern():
+    """oracle.as_f64 on bf16 storage against torch's own bf16 type: all 65,536 bit patterns give
+    the same value (and sign of zero); NaN patterns give NaN."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN
+        got = oracle.as_f64(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127  # exponent all ones with a non-zero mantissa, both signs
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
 def test_cache_write_rejects_bad_slots():
     pool = np.zeros((2, 1, 16, 4), np.float32)
     k = np.ones((2, 1, 4), np.float32)
@@ -190,34 +204,36 @@ def test_chunked_prefill_matches_torch_sdpa_and_one_pass():
     assert np.max(np.abs(chunked - one)) <= 1e-12
 
 
-def test_page_example_fp32_prints_true():
-    """The page's own fp32 experiment, rewritten: seed 0, 1000 tokens, 8 heads x 64, chunks of 256."""
-    g = _golden("p3_chunked_prefill_example.json")["setup"]
-    torch.manual_seed(g["seed"])
-    n, ch = g["prompt_len"], g["chunk"]
-    q, k, v = torch.randn(3, 1, g["heads"], n, g["head_dim"]).unbind(0)
-    full = F.scaled_dot_product_attention(q, k, v, is_causal=True)
-    parts = []
-    for s in range(0, n, ch):
-        e = min(s + ch, n)
-        vis = torch.arange(e)[None, :] <= torch.arange(s, e)[:, None]
-        parts.append(F.scaled_dot_product_attention(q[..., s:e, :], k[..., :e, :], v[..., :e, :], attn_mask=vis))
-    chunked = torch.cat(parts, dim=2)
-    assert len(parts) == 4
-    assert torch.allclose(full, chunked, atol=g["atol"])
-    # The oracle in fp64 on the same values (fp32 storage) agrees with torch's fp32 one-pass result.
-    hd = g["head_dim"]
-    qn = q[0].permute(1, 0, 2).contiguous().numpy()  # [n, H, hd]
-    kn = k[0].permute(1, 0, 2).contiguous().numpy()
-    vn = v[0].permute(1, 0, 2).contiguous().numpy()
+def test_chunked_fp32_equals_one_pass_at_the_page_tolerance():
+    """The property the Chunked Prefill page's example prints (True): the prompt cut into the page's
+    chunks, each chunk attending over the cache after its own K/V was stored, gives the one-pass
+    causal result within the page's fp32 tolerance.  Chunk bounds, sizes, head shape and tolerance
+    come from the fixture; the values are a seeded fp32 N(0,1) draw.  The chunks run through the
+    oracle over a paged pool with shuffled block ids (dead slots NaN); the one-pass result is
+    torch's fp32 attention with its built-in causal mask."""
+    g = _golden("p3_chunked_prefill_example.json")
+    setup = g["setup"]
+    n, H, hd = setup["prompt_len"], setup["heads"], setup["head_dim"]
+    bounds = np.cumsum([0] + g["chunk_lengths"])
+    assert bounds[-1] == n and len(g["chunk_lengths"]) == g["printed"]["num_chunks"]
+    rng = np.random.default_rng(setup["seed"])
+    q, k, v = (rng.standard_normal((n, H, hd)).astype(np.float32) for _ in range(3))
     nb = -(-n // 16)
-    bt = np.arange(nb, dtype=np.int32)[None, :]
-    pool = np.zeros((nb, g["heads"], 16, hd), np.float32)
-    slots = oracle.slot_mapping(bt, np.array([0, n], np.int32), np.array([0], np.int32), 16)
-    kp, vp = oracle.cache_write(pool, pool, kn, vn, slots)
-    got = oracle.prefill_chunk(qn, np.array([0, n], np.int32), np.array([0], np.int32), kp, vp, bt,
-                               1.0 / math.sqrt(hd), "f32")
-    np.testing.assert_allclose(got, full[0].permute(1, 0, 2).double().numpy(), rtol=0, atol=1e-5)
+    nblk = nb + 5
+    bt = rng.permutation(nblk)[:nb].astype(np.int32)[None, :]
+    kp = np.full((nblk, H, 16, hd), np.nan, np.float32)
+    vp = kp.copy()
+    chunks = []
+    for s, e in zip(bounds[:-1], bounds[1:]):
+        cu, start = np.array([0, e - s], np.int32), np.array([s], np.int32)
+        kp, vp = oracle.cache_write(kp, vp, k[s:e], v[s:e], oracle.slot_mapping(bt, cu, start, 16))
+        chunks.append(oracle.prefill_chunk(q[s:e], cu, start, kp, vp, bt, 1.0 / math.sqrt(hd), "f32"))
+    chunked = np.concatenate(chunks)
+    heads_first = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))
+    one = F.scaled_dot_product_attention(heads_first(q), heads_first(k), heads_first(v), is_causal=True)
+    one = one.numpy().transpose(1, 0, 2).astype(np.float64)
+    assert np.isfinite(chunked).all()
+    assert np.allclose(chunked, one, rtol=0, atol=setup["atol"]) == g["printed"]["same_as_one_pass"]
 
 
 def _decimal_attention(q, K, V, scale_sq_inv):
@@ -359,6 +375,7 @@ def test_split_partials_combine_to_unsplit(split):
 def _run_pins():
     failures = 0
     for fn in (test_block_table_example_engine_core_page, test_gather_small_scale_instance,
+               test_bf16_widening_matches_torch_over_every_pattern,
                test_tiny_decode_matches_torch_sdpa_fp64, test_gqa_decode_matches_torch_sdpa_enable_gqa,
                test_closed_forms):
         try:
@@ -378,7 +395,7 @@ def test_pins_pass_on_the_oracle_as_written():
 
 
 @pytest.mark.parametrize("mutation", ["slot_offset", "kv_head_modulo", "causal_off_by_one", "gather_order",
-                                      "scale_dropped"])
+                                      "scale_dropped", "bf16_no_widening"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     if mutation == "slot_offset":
         monkeypatch.setattr(pa, "physical_block", lambda row, p, b: int(row[p // b - 1 if p >= b else 0]))
@@ -394,6 +411,17 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             nb = -(-int(length) // b)
             return orig(pool, np.concatenate([row[:nb][::-1], row[nb:]]), length)
         monkeypatch.setattr(pa, "gather", reversed_blocks)
+    elif mutation == "bf16_no_widening":
+        orig_f64 = pa.as_f64
+
+        def narrow_shift(x, dtype):
+            if dtype != "bf16":
+                return orig_f64(x, dtype)
+            # The shift done in 16 bits: the pattern is lost before it reaches the fp32 exponent.
+            bits = (np.asarray(x, dtype=np.uint16) << np.uint16(16)).astype(np.uint32)
+            return bits.view(np.float32).astype(np.float64)
+        monkeypatch.setattr(pa, "as_f64", narrow_shift)
+        monkeypatch.setattr(oracle, "as_f64", narrow_shift)
     elif mutation == "scale_dropped":
         orig_sa = pa.softmax_attention
         monkeypatch.setattr(pa, "softmax_attention", lambda q, K, V, scale, vis: orig_sa(q, K, V, 1.0, vis))
