@@ -73,7 +73,9 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 2,         /* dtype, head_dim, head ratio or block size outside the list above */
   PKV_ERR_WORKSPACE_TOO_SMALL = 3, /* decode workspace below pkv_decode_workspace_bytes() */
   PKV_ERR_HIP = 4,                 /* a kernel launch failed */
-  PKV_ERR_NO_SPACE = 5             /* block manager: not enough free blocks (state left unchanged) */
+  PKV_ERR_NO_SPACE = 5,            /* block manager: not enough free blocks (state left unchanged) */
+  PKV_ERR_SCRATCH_TOO_SMALL = 6    /* pkv_paged_attn_decode_noalloc: the shapes need more than
+                                      PKV_NOALLOC_SCRATCH_BYTES of workspace */
 } pkv_status;
 
 /* Element types.  FP8_E4M3 is the OCP 8-bit floating point E4M3 encoding (1 sign, 4 exponent bits
@@ -184,6 +186,29 @@ pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* que
                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, float scale,
                                  pkv_dtype dtype, int32_t split_tokens, void* workspace, size_t workspace_bytes,
                                  int32_t* err_flag, void* stream);
+
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Computes exactly what
+ * pkv_paged_attn_decode computes (the same kernels, the same split size for the same arguments),
+ * with its workspace taken from a static device array of PKV_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on, for the life of the process.
+ *   Arguments as for pkv_paged_attn_decode, without workspace / workspace_bytes; BF16 or F32 pools.
+ *   PKV_ERR_SCRATCH_TOO_SMALL (nothing launched) when pkv_decode_workspace_bytes() for these shapes
+ *   and split size exceeds PKV_NOALLOC_SCRATCH_BYTES; PKV_ERR_HIP if the array's device address
+ *   cannot be obtained.  The caller still owns query, out, pools and tables.
+ *   All calls on one GPU share the array and it keeps the last call's contents (no call needs it
+ *   cleared): calls that overlap on one GPU (several streams or host threads at once) race and
+ *   give undefined results; serialise them, or use pkv_paged_attn_decode with a workspace each.
+ *   The call performs no hipMalloc / hipFree and no other allocating HIP or library routine.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+pkv_status pkv_paged_attn_decode_noalloc(void* out, pkv_dtype out_dtype, const void* query, const void* key_pool,
+                                         const void* value_pool, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t num_blocks, float scale, pkv_dtype dtype, int32_t split_tokens,
+                                         int32_t* err_flag, void* stream);
 
 /*
  * Chunked-prefill attention ([Chunked-Prefill], section on how chunked prefill works and its

@@ -27,7 +27,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, NO_SPACE = 0, 1, 2, 3, 4, 5
+OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR, NO_SPACE, SCRATCH_TOO_SMALL = 0, 1, 2, 3, 4, 5, 6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 FLAG_BAD_BLOCK, FLAG_BAD_SLOT, FLAG_BAD_LENGTH, FLAG_SYNC_TIMEOUT = 1, 2, 4, 8
 BLOCK_SIZE = 16
@@ -49,6 +50,8 @@ _SIGS = {
                                                 _i32, _f32, _f32, _f32, _vp, _i32, _i32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_paged_attn_decode": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                                      _i32, _i32, _vp, _sz, _vp, _vp]),
+    "pkv_paged_attn_decode_noalloc": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                             _f32, _i32, _i32, _vp, _vp]),
     "pkv_paged_attn_prefill_chunk": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "pkv_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -437,6 +440,33 @@ def paged_attn_decode(query: torch.Tensor, key_pool: torch.Tensor, value_pool: t
                                       nblk, float(scale), _dtype_code(key_pool), int(split_tokens),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _ptr(err_flag), _stream(query.device)), "pkv_paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_noalloc(query: torch.Tensor, key_pool: torch.Tensor, value_pool: torch.Tensor,
+                              block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                              out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                              split_tokens: int = 0, err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """pkv_paged_attn_decode with the library's static scratch instead of a workspace; see
+    pkv_paged_attn_decode_noalloc.  Pass `out` to keep the call free of allocations (only the
+    output is allocated here when it is not given)."""
+    _need_gpu(query, key_pool, value_pool, block_tables, context_lens, out, err_flag)
+    _need_i32(block_tables, context_lens, err_flag)
+    nblk, bs, hkv, hd = _pool_dims(key_pool, value_pool)
+    if query.dim() != 3 or query.shape[2] != hd or query.dtype != key_pool.dtype or not query.is_contiguous():
+        raise ValueError("query must be contiguous [num_seqs, num_q_heads, head_dim] in the pool dtype")
+    B, hq, _ = query.shape
+    if context_lens.shape[0] != B or block_tables.shape[0] != B:
+        raise ValueError("batch sizes differ")
+    if out is None:
+        out = torch.empty((B, hq, hd), dtype=out_dtype, device=query.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (B, hq, hd):
+        raise ValueError("out must be contiguous [num_seqs, num_q_heads, head_dim]")
+    _check(_lib.pkv_paged_attn_decode_noalloc(_ptr(out), _dtype_code(out), _ptr(query), _ptr(key_pool),
+                                              _ptr(value_pool), _ptr(block_tables), block_tables.shape[1],
+                                              _ptr(context_lens), B, hq, hkv, hd, nblk, float(scale),
+                                              _dtype_code(key_pool), int(split_tokens), _ptr(err_flag),
+                                              _stream(query.device)), "pkv_paged_attn_decode_noalloc")
     return out
 
 

@@ -27,6 +27,9 @@
 //   * pkv_paged_attn_decode_prefix: the members of a shared prefix (§1.5) get the prefix attended
 //     once per KV head by MFMA prefix items placed in front of the decode workers of the same
 //     launch (mixed.hip); the reduce merges those partials with the members' own splits.
+#include <atomic>
+#include <mutex>
+
 #include "decode_dev.hpp"
 #include "prefill_dev.hpp"
 
@@ -705,4 +708,68 @@ extern "C" pkv_status pkv_paged_attn_decode_prefix_fp8(void* out, pkv_dtype out_
                             context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale,
                             PKV_DTYPE_FP8_E4M3, k_scale, v_scale, prefix_members, num_members, prefix_blocks,
                             split_tokens, workspace, workspace_bytes, err_flag, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate (code under HIP graph
+// capture, tight serving loops, harnesses that forbid allocation).  The work plan and the split
+// partials live in `scratch`, a file-scope device array of PKV_NOALLOC_SCRATCH_BYTES: every GPU the
+// library runs on holds its own copy until the process ends, and every call on that GPU shares it.
+// Host code never passes `scratch` itself (its host-side name is not a device address): the
+// array's address on each device is resolved once, with that device current, on the first call
+// there, and that pointer is what the kernels receive.  Nothing in it must start at zero: the plan
+// pass rewrites the header, the counters and the piece list on every call.
+
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (resolved once per device).
+pkv_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return PKV_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
+        return PKV_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attn_decode_noalloc(void* out, pkv_dtype out_dtype, const void* query,
+                                                    const void* key_pool, const void* value_pool,
+                                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                                    const int32_t* context_lens, int32_t num_seqs,
+                                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t num_blocks, float scale, pkv_dtype dtype,
+                                                    int32_t split_tokens, int32_t* err_flag, void* stream) {
+  if (dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_UNSUPPORTED;  // FP8 pools need their scales
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                 split_tokens);
+  if (need > PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH_TOO_SMALL;
+  // Invalid shapes (need == 0) and empty batches are answered by the argument checks alone.
+  if (need == 0 || num_seqs == 0)
+    return decode_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale, dtype, 1.f, 1.f, split_tokens,
+                       nullptr, 0, err_flag, stream);
+  void* ws = nullptr;
+  const pkv_status st = scratch_address(&ws);
+  if (st != PKV_OK) return st;
+  return decode_impl(out, out_dtype, query, key_pool, value_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, scale, dtype, 1.f, 1.f, split_tokens,
+                     ws, PKV_NOALLOC_SCRATCH_BYTES, err_flag, stream);
 }

@@ -11,6 +11,7 @@ extern "C" const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_WORKSPACE_TOO_SMALL: return "decode workspace too small";
     case PKV_ERR_HIP: return "HIP kernel launch failed";
     case PKV_ERR_NO_SPACE: return "not enough free blocks";
+    case PKV_ERR_SCRATCH_TOO_SMALL: return "shapes need more than the no-alloc decode's static scratch";
   }
   return "unknown status";
 }

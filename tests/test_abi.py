@@ -77,6 +77,16 @@ def test_host_validation_rejects_bad_arguments():
     assert dec(fake, 0, fake, fake, fake, fake, 64, fake, 2, 8, 8, 64, 10, 0.1, 1, 128, null, 0, null, null) == 3
     # Empty batch is a no-op.
     assert dec(null, 0, null, null, null, null, 8, null, 0, 8, 8, 64, 10, 0.1, 1, 0, null, 0, null, null) == 0
+    # The no-alloc decode: the same argument checks, and shapes beyond its static scratch refused
+    # before anything touches the GPU.
+    na = lib.pkv_paged_attn_decode_noalloc
+    assert na(null, 0, null, null, null, null, 8, null, 2, 8, 3, 64, 10, 0.1, 1, 0, null, null) == 1
+    assert na(null, 0, null, null, null, null, 8, null, 2, 8, 8, 96, 10, 0.1, 1, 0, null, null) == 2
+    assert na(null, 0, null, null, null, null, 8, null, 2, 8, 8, 64, 10, 0.1, 2, 0, null, null) == 2
+    assert na(null, 0, null, null, null, null, 8, null, 0, 8, 8, 64, 10, 0.1, 1, 0, null, null) == 0
+    assert pkv.decode_workspace_bytes(1024, 64, 8, 128, 1024) > pkv.NOALLOC_SCRATCH_BYTES
+    assert na(null, 0, null, null, null, null, 1024, null, 1024, 64, 8, 128, 10, 0.1, 1, 0, null, null) == 6
+    assert "scratch" in pkv.status_string(pkv.SCRATCH_TOO_SMALL)
     # Prefill: bf16 only, head_dim list, null pointers.
     pre = lib.pkv_paged_attn_prefill_chunk
     assert pre(null, 0, null, null, null, null, null, null, 8, 1, 10, 8, 8, 64, 10, 1, 0.1, 0, null, 0, null, null) == 2
@@ -194,3 +204,10 @@ def test_header_documents_each_call(name):
     block = text[max(0, i - 2500):i]
     assert "/*" in block and any(tag in block for tag in ("Chunked Prefill", "Chunked-Prefill", "C13",
                                                           "vLLM-internals", "Engine-core"))
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    import paged_kv_cache_170_amd as pkv
+
+    m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m[1]) << int(m[2]) == pkv.NOALLOC_SCRATCH_BYTES
