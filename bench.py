@@ -8,11 +8,18 @@ A step is one pass of the whole path over the mixed chunked-prefill + decode wor
   4. prefill-chunk attention of the 512 rows over 16,384 cached + 512 causal positions,
 all enqueued on one stream with inputs resident in HBM.
 
+Timing: every timed step starts from cold caches.  Before each step (outside its events) a 1 GiB
+buffer is read, which evicts the L2s and the 256 MB MALL without leaving dirty lines behind;
+per-kernel times come from HIP events on the launch stream and are reported as median, p10 and
+p90.  The same steps run back to back without the flush ("hot") are reported beside them.
+
 Printed: one JSON line.  `value` is the decode KV-read bandwidth in GB/s over unique pool bytes
-(the shared prefix counted once); the prefill chunk's TFLOP/s and both fractions of peak are in
-`secondary`; `roofline` describes the kernel that takes the most time per step.  Per-kernel
-times come from HIP events on the launch stream.  `cpu_baseline` times the fp64 oracle on this
-host on the same inputs (decode of every sequence, prefill of a sample of rows).
+(the shared prefix counted once) at the median flushed decode call (plan, attention and reduce);
+the prefill chunk's TFLOP/s, both fractions of peak, the hot figures and the two small configs
+(tiny fp32 decode, 1000-token chunked prefill) are in `secondary`; `roofline` describes the
+kernel that takes the most time per step, at its average flushed duration.  `cpu_baseline` times
+the fp64 oracle on this host on the same inputs (decode of every sequence, prefill of a sample of
+rows), with the small configs' oracle times (all host threads and one thread) beside it.
 
 Other workloads (--workload): gqa_decode and long_decode (decode only), and shared_prefix (64
 sequences behind one 4,096-token cached prompt, decoded by the shared-prefix decode, with the
@@ -50,8 +57,13 @@ def parse():
                     help="KV pool storage: bf16, or E4M3 codes with per-pool scales (quantised from the bf16 "
                          "pools at setup; the step's new tokens go through the quantising write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra untimed-for-value steps, each after a 1 GiB write that flushes L2 and MALL")
+    ap.add_argument("--hot-steps", type=int, default=-1,
+                    help="steps run back to back without the flush, reported beside the flushed ones "
+                         "(default: as many as --steps; 0 skips them)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time the steps without the cache flush (for profilers that count every launch)")
+    ap.add_argument("--no-small-configs", action="store_true",
+                    help="skip the tiny-decode and chunked-prefill configs reported in secondary")
     ap.add_argument("--cpu-sample-rows", type=int, default=64, help="prefill rows timed in the oracle baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain fp32 copy kernel over this many MiB (a known-size reference "
@@ -75,9 +87,9 @@ def sources_hash(names):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel_key: str, src):
-    """HBM bytes per launch from a committed counter summary, if it was taken on these sources
-    (src: one .hip file or a list of them)."""
+def counter_record(kernel_key: str, src):
+    """A committed counter summary (profiles/counters_<kernel>_<workload>.json), if it was taken
+    on these sources (src: one .hip file or a list of them); else None."""
     path = os.path.join(PROFILES, f"counters_{kernel_key}.json")
     if not os.path.exists(path):
         return None
@@ -85,7 +97,13 @@ def counter_traffic(kernel_key: str, src):
         rec = json.load(f)
     if rec.get("sources_hash") != sources_hash([src] if isinstance(src, str) else list(src)):
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def counter_traffic(kernel_key: str, src):
+    """HBM bytes per launch from a committed counter summary taken on these sources."""
+    rec = counter_record(kernel_key, src)
+    return None if rec is None else rec.get("traffic_bytes_per_launch")
 
 
 def unique_kv_bytes(case) -> int:
@@ -256,43 +274,56 @@ def main():
                                              out=p_out, workspace=p_ws)
         mark(4)
 
+    # The flush: a 1 GiB read evicts the L2s and the 256 MB MALL and leaves only clean lines, so no
+    # write-back of the flush itself lands inside the next step.
+    flush_buf = None if args.no_flush else torch.ones(1 << 28, dtype=torch.int32, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            torch.amax(flush_buf)
+
+    def collect(evs):
+        out = {n: [] for n in names + ["step"]}
+        for ev in evs:
+            for i, n in enumerate(names):
+                out[n].append(ev[i].elapsed_time(ev[i + 1]))
+            out["step"].append(ev[0].elapsed_time(ev[len(names)]))
+        return out
+
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        flush()
         step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: [] for n in names}
-    for ev in events:
-        for i, n in enumerate(names):
-            per[n].append(ev[i].elapsed_time(ev[i + 1]))
+    per = collect(events)
     avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
     med_ms = {n: float(np.median(v)) for n, v in per.items()}
     ms_per_step = wall * 1e3 / args.steps
-    print(f"[bench] {args.steps} steps in {wall:.3f}s; per-kernel avg ms "
-          + ", ".join(f"{n}={avg_ms[n]:.4f}" for n in names), file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} {'flushed ' if flush_buf is not None else ''}steps in {wall:.3f}s; per-kernel "
+          "median ms " + ", ".join(f"{n}={med_ms[n]:.4f}" for n in names), file=sys.stderr, flush=True)
 
     def spread(v):
         return {"p10": float(np.percentile(v, 10)), "p50": float(np.median(v)), "p90": float(np.percentile(v, 90))}
 
-    # Cold-cache timings (outside the timed region): before each step a 1 GiB write evicts the
-    # L2s and the 256 MB MALL, so every kernel starts from HBM.
-    cold = {n: [] for n in names}
-    if args.cold_steps > 0:
-        flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_steps)]
-        for k in range(args.cold_steps):
-            flush.zero_()
-            step(cev[k])
+    # The same steps back to back, caches warm from the previous step.
+    hot_steps = args.steps if args.hot_steps < 0 else args.hot_steps
+    hot = None
+    if hot_steps > 0:
+        hev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(hot_steps)]
+        for k in range(hot_steps):
+            step(hev[k])
         torch.cuda.synchronize()
-        for ev in cev:
-            for i, n in enumerate(names):
-                cold[n].append(ev[i].elapsed_time(ev[i + 1]))
-        del flush
+        hot = collect(hev)
+        print(f"[bench] {hot_steps} hot steps; per-kernel median ms "
+              + ", ".join(f"{n}={float(np.median(hot[n])):.4f}" for n in names), file=sys.stderr, flush=True)
+    del flush_buf
 
     # Bandwidth a plain read stream reaches on this device: read the whole key pool (>= 1 GB).
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -365,8 +396,10 @@ def main():
             pt = min(pt, e0.elapsed_time(e1) / 10)
         step()
         torch.cuda.synchronize()
-        plain_info = {"plain_decode_ms": pt, "prefix_decode_ms": avg_ms["decode"],
-                      "speedup": pt / avg_ms["decode"], "max_abs_diff": float((p_out - d_out).abs().max()),
+        # Both back to back (warm caches): the plain decode's best of three, the prefix decode's hot median.
+        pfx_ms = float(np.median(hot["decode"])) if hot is not None else avg_ms["decode"]
+        plain_info = {"plain_decode_ms": pt, "prefix_decode_ms": pfx_ms,
+                      "speedup": pt / pfx_ms, "max_abs_diff": float((p_out - d_out).abs().max()),
                       "members": int(len(dec.notes["members"])), "prefix_blocks": pfx_blocks}
         del p_out, pws
 
@@ -405,10 +438,14 @@ def main():
     bm_info = {"sequences": dec.num_seqs, "prefix_hits": hits, "us_per_operation": bm_us}
 
     dec_bytes, dec_kv_unique, dec_kv_logical = decode_algorithmic_bytes(dec, kv_elem=1 if fp8 else None)
-    dec_s = avg_ms["decode"] * 1e-3
+    # Headline: the median flushed decode call (plan, attention, reduce).
+    dec_s = med_ms["decode"] * 1e-3
     dec_gbs = dec_bytes / dec_s / 1e9
     secondary = {
-        "decode_ms": avg_ms["decode"],
+        "timing": ("flushed: a 1 GiB read before each step evicts L2 and MALL; medians over the timed steps"
+                   if not args.no_flush else "no flush: steps back to back"),
+        "decode_ms": med_ms["decode"],
+        "decode_ms_avg": avg_ms["decode"],
         "decode_gbs_unique": dec_gbs,
         "decode_frac_hbm_peak": dec_gbs / HBM_PEAK_GBS,
         "decode_gbs_logical": (dec_bytes - dec_kv_unique + dec_kv_logical) / dec_s / 1e9,
@@ -422,43 +459,61 @@ def main():
         "block_manager_host": bm_info,
     }
     ran = [n for n in names if (has_write or n not in ("slot_mapping", "cache_write")) and (pre is not None or n != "prefill")]
-    secondary["kernel_ms_hot"] = {n: spread(per[n]) for n in ran}
-    if args.cold_steps > 0:
-        secondary["kernel_ms_cold"] = {n: spread(cold[n]) for n in ran}
-        secondary["decode_gbs_unique_cold"] = dec_bytes / (float(np.median(cold["decode"])) * 1e-3) / 1e9
+    secondary["kernel_ms"] = {n: spread(per[n]) for n in ran + ["step"]}
+    hot_info = None
+    if hot is not None:
+        hot_info = {"kernel_ms": {n: spread(hot[n]) for n in ran + ["step"]}}
+        hdec = float(np.median(hot["decode"]))
+        hot_info.update({"decode_ms": hdec, "decode_gbs_unique": dec_bytes / (hdec * 1e-3) / 1e9,
+                         "decode_frac_hbm_peak": dec_bytes / (hdec * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    secondary["hot"] = hot_info
     # The shared-prefix decode also runs the fused launch (mixed.hip) and the prefill body.
     dec_src = ["decode.hip", "mixed.hip", "prefill.hip"] if pfx else "decode.hip"
-    kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs, HBM_PEAK_GBS, "GB/s", dec_src)}
+    # Roofline of each kernel at its average flushed duration over the timed steps.
+    dec_gbs_avg = dec_bytes / (avg_ms["decode"] * 1e-3) / 1e9
+    kernels = {"decode": (avg_ms["decode"], "hbm", dec_bytes, dec_gbs_avg, HBM_PEAK_GBS, "GB/s", dec_src)}
+    tag = args.workload + ("_fp8" if fp8 else "")
     if pre is not None:
         fl = prefill_flops(pre)
-        pre_tf = fl / (avg_ms["prefill"] * 1e-3) / 1e12
-        secondary.update({"prefill_ms": avg_ms["prefill"], "prefill_flop": fl, "prefill_tflops": pre_tf,
-                          "prefill_frac_mfma_peak": pre_tf / BF16_MFMA_PEAK_TFLOPS})
-        if args.cold_steps > 0:
-            secondary["prefill_tflops_cold"] = fl / (float(np.median(cold["prefill"])) * 1e-3) / 1e12
-        kernels["prefill"] = (avg_ms["prefill"], "mfma", fl, pre_tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s", "prefill.hip")
+        pre_tf = fl / (med_ms["prefill"] * 1e-3) / 1e12
+        secondary.update({"prefill_ms": med_ms["prefill"], "prefill_ms_avg": avg_ms["prefill"], "prefill_flop": fl,
+                          "prefill_tflops": pre_tf, "prefill_frac_mfma_peak": pre_tf / BF16_MFMA_PEAK_TFLOPS})
+        if hot is not None:
+            hpre = float(np.median(hot["prefill"]))
+            hot_info.update({"prefill_ms": hpre, "prefill_tflops": fl / (hpre * 1e-3) / 1e12,
+                             "prefill_frac_mfma_peak": fl / (hpre * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS})
+        pre_tf_avg = fl / (avg_ms["prefill"] * 1e-3) / 1e12
+        kernels["prefill"] = (avg_ms["prefill"], "mfma", fl, pre_tf_avg, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s", "prefill.hip")
+        # Matrix-core counters of the prefill kernel (committed summary of a rocprofv3 pass on these sources).
+        rec = counter_record(f"prefill_{tag}", "prefill.hip")
+        secondary["prefill_mfma_counters"] = None if rec is None else rec.get("mfma")
     if has_write:
         # read the new rows (bf16 or fp32) and write them into the pools (E4M3: one byte each)
         wb = (2 * wcase.num_new_tokens * wcase.num_kv_heads * wcase.head_dim * (wcase.elem_bytes + (1 if fp8 else wcase.elem_bytes))
               + 4 * wcase.num_new_tokens)
-        secondary.update({"cache_write_ms": avg_ms["cache_write"], "slot_mapping_ms": avg_ms["slot_mapping"],
-                          "cache_write_gbs": wb / (avg_ms["cache_write"] * 1e-3) / 1e9})
+        secondary.update({"cache_write_ms": med_ms["cache_write"], "slot_mapping_ms": med_ms["slot_mapping"],
+                          "cache_write_gbs": wb / (med_ms["cache_write"] * 1e-3) / 1e9})
     dominant = max(kernels, key=lambda k: kernels[k][0])
     ms, bound, work, achieved, peak, unit, src = kernels[dominant]
-    tag = args.workload + ("_fp8" if fp8 else "")
     roofline = {"kernel": dominant, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": counter_traffic(f"{dominant}_{tag}", src),
                 "work_per_launch": work, "avg_launch_ms": ms}
     for k, (ms_k, bound_k, work_k, ach_k, peak_k, unit_k, src_k) in kernels.items():
         secondary[f"roofline_{k}"] = {"bound": bound_k, "achieved": ach_k, "peak": peak_k, "unit": unit_k,
-                                      "frac": ach_k / peak_k,
+                                      "frac": ach_k / peak_k, "avg_launch_ms": ms_k,
                                       "traffic": counter_traffic(f"{k}_{tag}", src_k)}
+    small = None
+    if not args.no_small_configs and not fp8 and args.workload == "mixed_step":
+        small = small_configs(pkv, torch, dev, flush_bytes=0 if args.no_flush else 1 << 30)
+        secondary["small_configs"] = small["gpu"]
 
     cpu = None
     if fp8:
         print("[bench] cpu baseline is reported for the bf16 pools only", file=sys.stderr, flush=True)
     elif not args.no_cpu_baseline:
         cpu = cpu_baseline(dec, pre, kp, vp, has_write, args, torch)
+        if small is not None:
+            cpu["small_configs"] = small_configs_oracle(small)
 
     config = {"workload": args.workload, "num_seqs_decode": dec.num_seqs, "q_heads": dec.num_q_heads,
               "kv_heads": dec.num_kv_heads, "head_dim": dec.head_dim, "block_size": 16,
@@ -478,6 +533,143 @@ def main():
             "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
             "kernel_ms_median": med_ms}
     print(json.dumps(line), flush=True)
+
+
+def small_configs(pkv, torch, dev, flush_bytes, runs=20):
+    """The two small configs on the GPU: the tiny fp32 decode (4 sequences, contexts 17/50/100/128,
+    8 heads x 64) and the 1000-token chunked prefill (8 heads x 64, bf16, chunks 256/256/256/232).
+    A run writes the new tokens (slot mapping + cache write) and attends (the decode; the four
+    chunks, each written before its attention).  Median over `runs` runs, each after the flush,
+    of the attention time and of the whole run (HIP events).  Both are launch-bound: a handful of
+    microseconds per call."""
+    import workloads as wl
+
+    stream = torch.cuda.current_stream(dev)
+    flush_buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device=dev) if flush_bytes else None
+
+    def td(a, bf=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf else t).to(dev)
+
+    def timed(fn, marks):
+        res = []
+        for r in range(runs + 2):
+            if flush_buf is not None:
+                torch.amax(flush_buf)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(marks)]
+            fn(ev)
+            torch.cuda.synchronize()
+            if r >= 2:
+                res.append(ev)
+        return res
+
+    # Tiny decode (fp32).
+    c1 = wl.tiny_decode(poison=False)
+    kp, vp = td(c1.key_pool), td(c1.value_pool)
+    bt, ctx = td(c1.block_tables), td(c1.context_lens)
+    cu, st = td(c1.new_cu_lens), td(c1.new_start_pos)
+    kn, vn, q = td(c1.key_new), td(c1.value_new), td(c1.query)
+    slots = torch.empty(c1.num_new_tokens, dtype=torch.int32, device=dev)
+    out = torch.empty((c1.num_seqs, c1.num_q_heads, c1.head_dim), dtype=torch.float32, device=dev)
+    ws = pkv.decode_workspace(q, c1.num_kv_heads, c1.max_blocks_per_seq)
+    max_new = int(np.diff(c1.new_cu_lens).max())
+
+    def run_c1(ev):
+        ev[0].record(stream)
+        pkv.slot_mapping(bt, cu, st, max_new, c1.num_blocks, out=slots)
+        pkv.cache_write(kn, vn, kp, vp, slots)
+        ev[1].record(stream)
+        pkv.paged_attn_decode(q, kp, vp, bt, ctx, c1.scale, out=out, workspace=ws)
+        ev[2].record(stream)
+
+    evs = timed(run_c1, 3)
+    att = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    whole = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    c1_bytes, _, _ = decode_algorithmic_bytes(c1)
+    gpu = {"tiny_decode": {"decode_ms": att, "run_ms": whole, "decode_bytes": c1_bytes,
+                           "decode_gbs": c1_bytes / (att * 1e-3) / 1e9,
+                           "decode_frac_hbm_peak": c1_bytes / (att * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+    # Chunked prefill equivalence (bf16).
+    c2 = wl.chunked_prefill(poison=False)
+    chunks = c2.notes["chunks"]
+    kp2, vp2 = td(c2.key_pool, True), td(c2.value_pool, True)
+    bt2 = td(c2.block_tables)
+    kn2, vn2, q2 = td(c2.key_new, True), td(c2.value_new, True), td(c2.query, True)
+    cus = [td(np.array([0, e - s], np.int32)) for s, e in chunks]
+    offs = [td(np.array([s], np.int32)) for s, _ in chunks]
+    slots2 = [torch.empty(e - s, dtype=torch.int32, device=dev) for s, e in chunks]
+    out2 = torch.empty((c2.query.shape[0], c2.num_q_heads, c2.head_dim), dtype=torch.float32, device=dev)
+    ws2 = pkv.prefill_workspace(q2, 1, max(e - s for s, e in chunks), c2.max_blocks_per_seq)
+
+    def run_c2(ev):
+        for i, (s, e) in enumerate(chunks):
+            ev[2 * i].record(stream)
+            pkv.slot_mapping(bt2, cus[i], offs[i], e - s, c2.num_blocks, out=slots2[i])
+            pkv.cache_write(kn2[s:e], vn2[s:e], kp2, vp2, slots2[i])
+            ev[2 * i + 1].record(stream)
+            pkv.paged_attn_prefill_chunk(q2[s:e], cus[i], offs[i], kp2, vp2, bt2, e - s, c2.scale, causal=True,
+                                         out=out2[s:e], workspace=ws2)
+        ev[2 * len(chunks)].record(stream)
+
+    evs = timed(run_c2, 2 * len(chunks) + 1)
+    n = len(chunks)
+    att = float(np.median([sum(e[2 * i + 1].elapsed_time(e[2 * i + 2]) for i in range(n)) for e in evs]))
+    whole = float(np.median([e[0].elapsed_time(e[2 * n]) for e in evs]))
+    fl = 0
+    for s, e in chunks:
+        L = e - s
+        fl += 4 * c2.head_dim * c2.num_q_heads * (L * s + L * (L + 1) // 2)
+    gpu["chunked_prefill"] = {"chunks": [e - s for s, e in chunks], "prefill_ms": att, "run_ms": whole,
+                              "prefill_flop": fl, "prefill_tflops": fl / (att * 1e-3) / 1e12,
+                              "prefill_frac_mfma_peak": fl / (att * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+    del flush_buf
+    return {"gpu": gpu, "c1": c1, "c2": c2, "c1_bytes": c1_bytes, "c2_flop": fl}
+
+
+def small_configs_oracle(small):
+    """The oracle on the two small configs, with every host thread BLAS offers and with one thread
+    (median of 3 runs each): the tiny decode after the oracle's own cache write, and the four
+    chunks of the chunked prefill, each written before its attention."""
+    import oracle
+
+    c1, c2 = small["c1"], small["c2"]
+
+    def run_c1():
+        slots = oracle.slot_mapping(c1.block_tables, c1.new_cu_lens, c1.new_start_pos, 16)
+        kp, vp = oracle.cache_write(c1.key_pool, c1.value_pool, c1.key_new, c1.value_new, slots)
+        oracle.decode(c1.query, kp, vp, c1.block_tables, c1.context_lens, c1.scale, "f32")
+
+    def run_c2():
+        kp, vp = c2.key_pool, c2.value_pool
+        for s, e in c2.notes["chunks"]:
+            cu = np.array([0, e - s], np.int32)
+            off = np.array([s], np.int32)
+            slots = oracle.slot_mapping(c2.block_tables, cu, off, 16)
+            kp, vp = oracle.cache_write(kp, vp, c2.key_new[s:e], c2.value_new[s:e], slots)
+            oracle.prefill_chunk(c2.query[s:e], cu, off, kp, vp, c2.block_tables, c2.scale, "bf16")
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+        return float(np.median(ts))
+
+    def measure():
+        t1, t2 = med3(run_c1), med3(run_c2)
+        return {"cores": blas_threads(), "tiny_decode": {"s": t1, "gbs": small["c1_bytes"] / t1 / 1e9},
+                "chunked_prefill": {"s": t2, "gflops": small["c2_flop"] / t2 / 1e9}}
+
+    res = {"all_threads": measure()}
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        return res
+    with threadpool_limits(limits=1):
+        res["one_thread"] = measure()
+    return res
 
 
 def cpu_baseline(dec, pre, kp, vp, has_write, args, torch):
