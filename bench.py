@@ -337,6 +337,20 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = 5 * kp.numel() * kp.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
+    # Rate a kernel of pure bf16 MFMA work reaches on this device (every SIMD issuing independent
+    # 32x32x16 MFMAs and nothing else), run for about as long as the prefill chunk takes.
+    mfma_loop = None
+    if pre is not None:
+        msink = torch.zeros(1, dtype=torch.float32, device=dev)
+        pkv.mfma_peak_probe(2000, msink)
+        e0.record(stream)
+        mflop = sum(pkv.mfma_peak_probe(2000, msink) for _ in range(5))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mt = e0.elapsed_time(e1) / 5
+        mfma_loop = {"ms_per_call": mt, "tflops": mflop / 5 / (mt * 1e-3) / 1e12}
+        mfma_loop["frac_of_peak"] = mfma_loop["tflops"] / BF16_MFMA_PEAK_TFLOPS
+
     # Fused mixed-batch launch against the two separate attention calls (same inputs, same pools).
     fused_info = None
     if pre is not None:
@@ -477,7 +491,9 @@ def main():
         fl = prefill_flops(pre)
         pre_tf = fl / (med_ms["prefill"] * 1e-3) / 1e12
         secondary.update({"prefill_ms": med_ms["prefill"], "prefill_ms_avg": avg_ms["prefill"], "prefill_flop": fl,
-                          "prefill_tflops": pre_tf, "prefill_frac_mfma_peak": pre_tf / BF16_MFMA_PEAK_TFLOPS})
+                          "prefill_tflops": pre_tf, "prefill_frac_mfma_peak": pre_tf / BF16_MFMA_PEAK_TFLOPS,
+                          "mfma_loop": mfma_loop,
+                          "prefill_frac_of_mfma_loop": pre_tf / mfma_loop["tflops"] if mfma_loop else None})
         if hot is not None:
             hpre = float(np.median(hot["prefill"]))
             hot_info.update({"prefill_ms": hpre, "prefill_tflops": fl / (hpre * 1e-3) / 1e12,

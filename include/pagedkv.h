@@ -509,6 +509,18 @@ uint64_t pkv_bm_block_hash(const void* state, int32_t block);
  */
 pkv_status pkv_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Matrix-core reference (not part of the attention path): one 512-thread workgroup per compute
+ * unit (two waves per SIMD), every wave issuing `iters` x 4 independent v_mfma_f32_32x32x16_bf16
+ * (32,768 flop each) on register operands and nothing else; *sink (a device float) is written
+ * only if the sums take a value they never take, so the work is kept but nothing is stored.  Its
+ * duration gives the bf16 MFMA rate a kernel of pure matrix work reaches on the device (its clock
+ * under that load included), against which the prefill's rate is compared.  The flop count of one
+ * call is cu_count x 8 waves x iters x 4 x 32,768.  iters must be positive.
+ */
+pkv_status pkv_mfma_peak_probe(int32_t iters, float* sink, void* stream);
+int32_t pkv_device_cu_count(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,6 +75,8 @@ _SIGS = {
     "pkv_sched_request_times": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "pkv_sched_itl": (_i64, [_vp, _vp, _i64]),
     "pkv_stream_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
+    "pkv_mfma_peak_probe": (_i32, [_i32, _vp, _vp]),
+    "pkv_device_cu_count": (_i32, []),
     "pkv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pkv_bm_state_bytes": (_sz, [_i32]),
     "pkv_bm_init": (_i32, [_vp, _sz, _i32, _i32, _vp]),
@@ -709,6 +711,14 @@ def paged_attn_mixed(key_pool: torch.Tensor, value_pool: torch.Tensor, scale: fl
                                      int(split_tokens), _ptr(workspace), ws_bytes, *_ws_args(pre_workspace),
                                      _ptr(err_flag), _stream(key_pool.device)), "pkv_paged_attn_mixed")
     return dec_out, pre_out
+
+
+def mfma_peak_probe(iters: int, sink: torch.Tensor) -> int:
+    """Pure bf16 MFMA work on every SIMD (matrix-core reference); returns the flops of the call.
+    `sink` is a device float tensor (written only in a case that never happens)."""
+    _need_gpu(sink)
+    _check(_lib.pkv_mfma_peak_probe(int(iters), _ptr(sink), _stream(sink.device)), "pkv_mfma_peak_probe")
+    return int(_lib.pkv_device_cu_count()) * 8 * int(iters) * 4 * 32768
 
 
 def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:

@@ -74,3 +74,39 @@ extern "C" pkv_status pkv_stream_read_probe(const void* buf, size_t bytes, uint3
                      static_cast<const uint4*>(buf), bytes / 16, sink);
   return pkv_host::launch_status();
 }
+
+// Matrix-core reference: independent MFMA chains on every SIMD, nothing else (see pagedkv.h).
+namespace {
+__global__ __launch_bounds__(512) void mfma_peak_kernel(int iters, float* __restrict__ sink) {
+  const int t = threadIdx.x;
+  pkv::bf16x8 x, y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = static_cast<__bf16>(0.01f * static_cast<float>(t + i));
+    y[i] = static_cast<__bf16>(0.02f * static_cast<float>(i - t));
+  }
+  pkv::floatx16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  for (int it = 0; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc[j], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[j][e];
+  if (s == -1.2345e-30f) sink[0] = s;  // never true; keeps the chains
+}
+}  // namespace
+
+extern "C" pkv_status pkv_mfma_peak_probe(int32_t iters, float* sink, void* stream) {
+  if (iters <= 0 || !sink) return PKV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(pkv_host::cu_count()), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     iters, sink);
+  return pkv_host::launch_status();
+}
+
+extern "C" int32_t pkv_device_cu_count(void) { return pkv_host::cu_count(); }
