@@ -40,8 +40,10 @@
  *   - Device pointers are device memory; int arguments are host values.  `stream` is a
  *     hipStream_t (NULL = the null stream).  Every call only enqueues work on `stream` and returns;
  *     buffers must stay alive until the stream reaches the call.  No call synchronises, allocates
- *     or keeps state between calls (the only cached state is each device's compute-unit count);
- *     the block manager (pkv_bm_*) is host code whose state lives in a caller-owned host buffer.
+ *     or keeps state between calls (the only cached state is each device's compute-unit count and,
+ *     for pkv_paged_attn_decode_noalloc, the device address of its static scratch); the block
+ *     manager (pkv_bm_*) is host code whose state lives in a caller-owned host buffer.  Since a
+ *     call only launches kernels on `stream`, calls can be captured in a HIP graph.
  *   - Calls return a pkv_status.  Argument errors are found on the host before any HIP call.
  *     PKV_ERR_HIP reports a failed launch (hipGetLastError).  No C++ exception crosses the ABI.
  *   - err_flag: if non-NULL (a device int32, zeroed by the caller), kernels check every block id
