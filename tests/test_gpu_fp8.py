@@ -163,6 +163,7 @@ FP8_DECODE = [
     (16, 4, 256, 1100, 1),
     (8, 8, 64, 300, 0),
     (16, 1, 128, 1300, 1),
+    (16, 1, 256, 1500, 1),
 ]
 
 
@@ -221,6 +222,8 @@ FP8_PREFILL = [
     (8, 1, 128, 300, 129, False),
     (4, 4, 256, 500, 200, True),
     (32, 2, 128, 1200, 513, True),
+    (16, 1, 256, 900, 200, True),
+    (8, 8, 64, 400, 150, True),
 ]
 
 
