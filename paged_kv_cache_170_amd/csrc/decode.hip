@@ -129,7 +129,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_f32_kernel(
     float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ out, int out_bf16, int32_t* err_flag) {
   constexpr int DPL = HD / kWave;  // head_dim elements per lane in P V
   constexpr int HALF = HD / 2;
-  constexpr int COMB = kMaxGroup * HD * 4 * kDecWaves;
+  constexpr int CP = DecCfg<HD>::CPITCH;  // merge row pitch in floats (merge_waves reads this layout)
+  constexpr int COMB = kMaxGroup * CP * 4 * kDecWaves;
   __shared__ __attribute__((aligned(16))) char smem[COMB + kDecWaves * kMaxGroup * 2 * 4 + kMaxGroup * HD * 4];
   float* q_lds = reinterpret_cast<float*>(smem + COMB + kDecWaves * kMaxGroup * 2 * 4);
 
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_f32_kernel(
   for (int hn = 0; hn < kMaxGroup; ++hn) {
     if (hn >= group) continue;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) comb_o[(wave * kMaxGroup + hn) * HD + lane + kWave * k] = o[hn][k];
+    for (int k = 0; k < DPL; ++k) comb_o[(wave * kMaxGroup + hn) * CP + lane + kWave * k] = o[hn][k];
     if (lane == 0) {
       comb_ml[(wave * kMaxGroup + hn) * 2] = m_run[hn];
       comb_ml[(wave * kMaxGroup + hn) * 2 + 1] = l_run[hn];

@@ -26,7 +26,9 @@ struct DecCfg {
   static constexpr int RPL = kWave / LPR;     // rows per wave-wide load
   static constexpr int VLD = kBlockSize / RPL;  // wave-wide loads per block and tensor
   static constexpr int STAGE = 2 * kBlockSize * (KPITCH + VPITCH);  // bytes per wave (two blocks of K and V)
-  static constexpr int COMB = kMaxGroup * HD * 4;                   // bytes per wave for the merge
+  static constexpr int CPITCH = HD + 4;  // floats per merge row: 4 more than HD, so the 16 rows a
+                                        // wave stores at once fall in different LDS banks
+  static constexpr int COMB = kMaxGroup * CPITCH * 4;               // bytes per wave for the merge
   static constexpr int BODY = (STAGE > COMB ? STAGE : COMB) * kDecWaves;
   static constexpr int LDS = BODY + kDecWaves * kMaxGroup * 2 * 4;
 };
@@ -39,6 +41,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v, bool 
 }
 
 // Merges the per-wave states held in LDS and writes either the final rows or the split partial.
+// comb_o holds wave w's row of query head hn at (w * kMaxGroup + hn) * DecCfg<HD>::CPITCH floats.
 // slots: partial slots per (sequence, query head) row of the workspace; final: the item is the
 // sequence's only part (one split and no shared-prefix partial), so it writes the normalised row.
 template <int HD>
@@ -55,7 +58,7 @@ __device__ __forceinline__ void merge_waves(const float* comb_o, const float* co
     for (int w = 0; w < kDecWaves; ++w) {
       const float mw = comb_ml[(w * kMaxGroup + hn) * 2];
       const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-      O += f * comb_o[(w * kMaxGroup + hn) * HD + d];
+      O += f * comb_o[(w * kMaxGroup + hn) * DecCfg<HD>::CPITCH + d];
       L += f * comb_ml[(w * kMaxGroup + hn) * 2 + 1];
     }
     const int h = g * group + hn;
@@ -349,7 +352,7 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   float* comb_ml = reinterpret_cast<float*>(smem + C::BODY);
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
-    *reinterpret_cast<floatx4*>(comb_o + (wave * kMaxGroup + n) * HD + 16 * mt + 4 * c) = acc[mt];
+    *reinterpret_cast<floatx4*>(comb_o + (wave * kMaxGroup + n) * C::CPITCH + 16 * mt + 4 * c) = acc[mt];
   if (c == 0) {
     comb_ml[(wave * kMaxGroup + n) * 2] = m_ref;
     comb_ml[(wave * kMaxGroup + n) * 2 + 1] = l_run;
