@@ -19,7 +19,8 @@ template <int HD, int E = 2>
 struct DecCfg {
   static constexpr int KK = HD / 32;          // k-steps of S^T = K Q^T over head_dim
   static constexpr int MT = HD / 16;          // 16-row tiles of O^T
-  static constexpr int KPITCH = HD * 2 + 16;  // bytes per staged K row (conflict-free 16-byte reads)
+  static constexpr int KPITCH = HD * 2 + 32;  // bytes per staged K row (no LDS bank conflicts on the
+                                              // staging writes or the 16-byte reads: counter-checked)
   static constexpr int VPITCH = HD * 2 + 32;  // bytes per staged V row (conflict-free transposed reads)
   static constexpr int EPL = 16 / E;          // pool elements per 16-byte lane load
   static constexpr int LPR = HD / EPL;        // lanes per row in a 16-byte-per-lane load
