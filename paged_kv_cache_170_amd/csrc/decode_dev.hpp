@@ -123,21 +123,19 @@ struct DecBuf {
 
 // One work item: positions [split * split_tokens, min(+split_tokens, ctx)) of sequence s, KV head g,
 // for all query heads of the group.  Called by all 256 threads of the workgroup.
-// What a work item needs before its first gather: where it is, its block ids (one per lane) and the
-// query fragment.  Loaded one item ahead so that these reads overlap the previous item's work.
+// What a work item needs before its first gather: where it is and its block ids (one per lane).
+// Loaded one item ahead so that these reads overlap the previous item's work.
 template <int HD>
 struct DecItem {
   int s, g, split, ctx, nsplit;
   int tbl0;  // first logical block of the item's table view (the prefix length for members, else 0)
   int my_id[2];   // block ids of the split: lane j holds blocks j and 64 + j
   int ref_id[2];  // the neighbouring sequence's ids at the same logical blocks (-2: none)
-  bf16x8 qf[DecCfg<HD>::KK];
 };
 
 template <int HD, bool CHECK>
 __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<HD>& it) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int n = lane & 15, c = lane >> 4;
   const int tok0 = it.split * A_.split_tokens;
   const int tok_end = min(tok0 + A_.split_tokens, it.ctx);
   const int32_t* table = A_.block_tables + static_cast<int64_t>(it.s) * A_.max_blocks + it.tbl0;
@@ -158,13 +156,6 @@ __device__ __forceinline__ void decode_item_prologue(const DecArgs& A_, DecItem<
   } else {
     it.ref_id[0] = it.ref_id[1] = -2;
   }
-  // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.  Columns
-  // n >= G repeat head G - 1 (their results are never written), so the loads need no select and
-  // nothing waits for them before the first MFMA.
-  const int hn = min(n, A_.group - 1);
-  const uint16_t* qrow = A_.query + (static_cast<int64_t>(it.s) * A_.num_q_heads + it.g * A_.group + hn) * HD + 8 * c;
-#pragma unroll
-  for (int kk = 0; kk < DecCfg<HD>::KK; ++kk) it.qf[kk] = as_bf16x8(ld16(qrow + 32 * kk));
 }
 
 // sync: barrier of the 256 threads running the item (the whole workgroup, or one half of a
@@ -179,7 +170,7 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
   const int s = it.s, g = it.g, split = it.split, ctx = it.ctx, nsplit = it.nsplit;
   const int my_id0 = it.my_id[0], my_id1 = it.my_id[1];
   const int ref_id0 = it.ref_id[0], ref_id1 = it.ref_id[1];
-  const bf16x8* qf = it.qf;
+  bf16x8 qf[DecCfg<HD>::KK];  // the query, loaded once the item's first gather is issued (below)
   const void* __restrict__ key_pool = A_.key_pool;
   const void* __restrict__ value_pool = A_.value_pool;
   const int num_q_heads = A_.num_q_heads, num_kv_heads = A_.num_kv_heads, group = A_.group;
@@ -338,10 +329,34 @@ __device__ __forceinline__ void decode_bf16_item(const DecArgs& A_, const DecIte
 
   DecBuf<HD, E> A;
   if (wave < units) load(wave, A);
+  {
+    // Q^T as the B operand: lane (n, c) holds head n, head_dim elements 32kk + 8c .. +7.  Columns
+    // n >= G repeat head G - 1 (their results are never written), so the loads need no select.
+    // Issued behind the first gather, the query arrives before that gather does; not carrying it
+    // over from the previous item keeps 16 (head_dim 128) to 32 registers free.
+    const int hn = min(n, group - 1);
+    const uint16_t* qrow = A_.query + (static_cast<int64_t>(s) * num_q_heads + g * group + hn) * HD + 8 * c;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) qf[kk] = as_bf16x8(ld16(qrow + 32 * kk));
+  }
   on_start();
-  for (int u = wave; u < units; u += kDecWaves) {
-    if (u != wave) load(u, A);
-    compute(u, A);
+  if constexpr (KV8) {
+    // E4M3 pools: a step's gathers are half the bytes of a bf16 step, so a wave keeps two steps in
+    // flight (the next step's gathers are issued before this step is computed).  bf16 pools
+    // already have enough bytes in flight, and a second buffer would push them into scratch.
+    DecBuf<HD, E> B2;
+    for (int u = wave; u < units; u += 2 * kDecWaves) {
+      if (u + kDecWaves < units) load(u + kDecWaves, B2);
+      compute(u, A);
+      if (u + kDecWaves >= units) break;
+      if (u + 2 * kDecWaves < units) load(u + 2 * kDecWaves, A);
+      compute(u + kDecWaves, B2);
+    }
+  } else {
+    for (int u = wave; u < units; u += kDecWaves) {
+      if (u != wave) load(u, A);
+      compute(u, A);
+    }
   }
 
   // Normaliser of head n: sum the four lane groups.
@@ -387,7 +402,7 @@ constexpr int kMaxClasses = 2048 / 32 + 1;
 // multiple of 8 and workgroups dealt round-robin over the 8 XCDs, queue q runs on XCD q % 8 and
 // holds only items with i % 8 == q % 8, so with Hkv = 8 each KV head stays on one XCD and blocks
 // shared between sequences stay in that XCD's L2.  The item after next is fetched while the
-// current item runs; the next item's block ids and query are loaded then too.
+// current item runs; the next item's block ids are loaded then too.
 // worker / nworkers: this worker's index in the persistent grid and the grid's size (the workgroup
 // index and count, or two workers per workgroup in the fused mixed-step kernel); smem holds
 // DecCfg<HD>::LDS bytes and fetched two ints, both private to the worker.
