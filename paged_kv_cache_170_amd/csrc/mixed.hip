@@ -26,7 +26,8 @@ struct MixCfg {
   static constexpr int LDS = (2 * DEC + 64 > PRE ? 2 * DEC + 64 : PRE);
 };
 
-template <int HD, bool CHECK, bool NARROW, bool KV8>
+// PACK: the prefill items' row layout (prefill_body); the shared-prefix rows do not depend on it.
+template <int HD, bool CHECK, bool NARROW, bool KV8, bool PACK>
 __global__ __launch_bounds__(kPreThreads) void mixed_step_kernel(DecArgs da, const int2* __restrict__ pieces,
                                                                  int32_t* __restrict__ plan, int queues, int dec_wgs,
                                                                  PreArgs pa, int pre_items, int pre_first) {
@@ -49,7 +50,8 @@ __global__ __launch_bounds__(kPreThreads) void mixed_step_kernel(DecArgs da, con
   } else {
     const int id = pre_first > 0 ? static_cast<int>(blockIdx.x) : b - dec_wgs;
     if (id < pre_items)
-      prefill_body<HD, CHECK, NARROW, KV8>(pa, id, pre_items, smem, reinterpret_cast<int*>(smem + PreCfg<HD>::LDS));
+      prefill_body<HD, CHECK, NARROW, KV8, PACK>(pa, id, pre_items, smem,
+                                                 reinterpret_cast<int*>(smem + PreCfg<HD>::LDS));
   }
 }
 
@@ -64,7 +66,7 @@ void pkv_dec::launch_prefix_decode(const DecArgs& da, const int2* pieces, int32_
   const int pre_first = (pre_items + 7) / 8 * 8;
   const unsigned grid = static_cast<unsigned>(pre_first + dec_wgs);
 #define PKV_PXD(HD, CHECK, NARROW, KV8)                                                                        \
-  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, KV8>), dim3(grid), dim3(kPreThreads), 0, st, da,   \
+  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, KV8, false>), dim3(grid), dim3(kPreThreads), 0, st, da, \
                      pieces, plan, queues, dec_wgs, pa, pre_items, pre_first)
 #define PKV_PXD_K(HD, CHECK, NARROW) \
   if (kv8) PKV_PXD(HD, CHECK, NARROW, true); else PKV_PXD(HD, CHECK, NARROW, false);
@@ -162,10 +164,14 @@ extern "C" pkv_status pkv_paged_attn_mixed(
   // Prefill part: the items (row tiles x key splits) of pkv_paged_attn_prefill_chunk.
   int pre_items = 0;
   int64_t pre_row_items = 0;
+  bool pack = false;
   PreArgs pa{};
   if (has_pre) {
-    const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
-    const int64_t row_items = static_cast<int64_t>(num_pre_seqs) * num_q_heads * q_tiles;
+    pack = pkv_pre::pack_rows(max_q_len, num_q_heads, num_kv_heads);
+    const int64_t q_tiles64 = pkv_pre::row_tiles(max_q_len, pack ? group : 1);
+    if (q_tiles64 > (1 << 22)) return PKV_ERR_UNSUPPORTED;
+    const int q_tiles = static_cast<int>(q_tiles64);
+    const int64_t row_items = static_cast<int64_t>(num_pre_seqs) * (pack ? num_kv_heads : num_q_heads) * q_tiles;
     const int ksplit = pkv_pre::ksplit_for(row_items, pre_max_blocks, head_dim, pkv_host::cu_count());
     const int64_t items = row_items * ksplit;
     if (items + dec_wgs > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
@@ -179,15 +185,18 @@ extern "C" pkv_status pkv_paged_attn_mixed(
                  causal != 0, scale_log2, vs, pre_out, ob, err_flag, ksplit,
                  ksplit > 1 ? reinterpret_cast<float*>(pw + lay.o) : nullptr,
                  ksplit > 1 ? reinterpret_cast<float*>(pw + lay.ml) : nullptr};
+    pa.pack = pack;
     pre_row_items = row_items;
   }
 
   const unsigned grid = static_cast<unsigned>(dec_wgs + pre_items);
-#define PKV_MIX(HD, CHECK, NARROW, KV8)                                                                   \
-  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, KV8>), dim3(grid), dim3(kPreThreads), 0, st, da, \
+#define PKV_MIX(HD, CHECK, NARROW, KV8, PACK)                                                                   \
+  hipLaunchKernelGGL((mixed_step_kernel<HD, CHECK, NARROW, KV8, PACK>), dim3(grid), dim3(kPreThreads), 0, st, da, \
                      pieces, plan, queues, dec_wgs, pa, pre_items, 0)
+#define PKV_MIX_P(HD, CHECK, NARROW, KV8) \
+  if (pack) PKV_MIX(HD, CHECK, NARROW, KV8, true); else PKV_MIX(HD, CHECK, NARROW, KV8, false);
 #define PKV_MIX_K(HD, CHECK, NARROW) \
-  if (kv8) PKV_MIX(HD, CHECK, NARROW, true); else PKV_MIX(HD, CHECK, NARROW, false);
+  if (kv8) { PKV_MIX_P(HD, CHECK, NARROW, true) } else { PKV_MIX_P(HD, CHECK, NARROW, false) }
 #define PKV_MIX_N(HD, CHECK) \
   if (narrow) { PKV_MIX_K(HD, CHECK, true) } else { PKV_MIX_K(HD, CHECK, false) }
 #define PKV_MIX_C(HD) \
@@ -196,6 +205,7 @@ extern "C" pkv_status pkv_paged_attn_mixed(
 #undef PKV_MIX_C
 #undef PKV_MIX_N
 #undef PKV_MIX_K
+#undef PKV_MIX_P
 #undef PKV_MIX
   if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
   if (has_dec && max_splits > 1) {

@@ -6,10 +6,13 @@
 // the chunked result equals one-pass causal prefill.  Non-causal rows see the whole chunk end.
 //
 // Design (gfx950, wave64):
-//   * a work item is 256 query rows of one query head (eight waves of 32 rows) and one key split;
-//     the 1-D grid is remapped so that each XCD (workgroups are dealt round-robin over the 8 XCDs)
-//     gets a contiguous run of items, i.e. the query heads of one KV head, which then share that
-//     KV head's K/V stream in the XCD's L2.
+//   * a work item is 256 rows (eight waves of 32 rows) and one key split.  The rows are the chunk
+//     positions of one query head, or, when that gives fewer row tiles (chunks short of 256
+//     positions, or well short of a multiple of it), the (position, query head) pairs of one KV
+//     head's group (row R = position R / G, query head g*G + R % G), so that each K/V tile an item
+//     stages serves all G heads; the 1-D grid is remapped so that each XCD (workgroups are dealt
+//     round-robin over the 8 XCDs) gets a contiguous run of items, whose K/V streams then meet in
+//     the XCD's L2.
 //   * when there are fewer row tiles than compute units, a row tile's key range is cut into up to
 //     eight splits of whole tile pairs, one workgroup each; every split writes its (o, m, l) partial
 //     to the workspace and prefill_merge_kernel combines them in split order after the launch.
@@ -44,14 +47,14 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PreArgs a) {
   const int w = blockIdx.x, r0 = blockIdx.y * kMergeRows;
   const int t = w % a.q_tiles;
   int q = w / a.q_tiles;
-  const int hi = q % a.group;
-  q /= a.group;
+  const int hp = a.pack ? a.group : 1;  // query heads sharing the rows
+  const int hi = a.pack ? 0 : q % a.group;
+  q = a.pack ? q : q / a.group;
   const int g = q % a.num_kv_heads;
   const int s = q / a.num_kv_heads;
-  const int h = g * a.group + hi;
   const int qlo = a.cu_q_lens[s];
-  const int L = a.cu_q_lens[s + 1] - qlo;
-  const int rows = min(kMergeRows, L - t * kPreTile - r0);
+  const int nrows = (a.cu_q_lens[s + 1] - qlo) * hp;
+  const int rows = min(kMergeRows, nrows - t * kPreTile - r0);
   if (rows <= 0) return;
   const int ks = a.ksplit;
   const int64_t base = static_cast<int64_t>(w) * ks * kPreTile + r0;
@@ -86,7 +89,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PreArgs a) {
     o.y *= inv;
     o.z *= inv;
     o.w *= inv;
-    const int64_t oi = (static_cast<int64_t>(qlo + t * kPreTile + r0 + r) * a.num_q_heads + h) * HD + d;
+    const int R = t * kPreTile + r0 + r;  // row: position R / hp, query head g*G + hi + R % hp
+    const int64_t oi = (static_cast<int64_t>(qlo + R / hp) * a.num_q_heads + g * a.group + hi + R % hp) * HD + d;
     if (a.out_bf16)
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + oi) = uint2{pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
     else
@@ -94,11 +98,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PreArgs a) {
   }
 }
 
-template <int HD, bool CHECK, bool NARROW, bool KV8>
+template <int HD, bool CHECK, bool NARROW, bool KV8, bool PACK>
 __global__ __launch_bounds__(kPreThreads) void prefill_bf16_kernel(PreArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[PreCfg<HD>::LDS];
   __shared__ int ids[kIdWindow];
-  prefill_body<HD, CHECK, NARROW, KV8>(a, blockIdx.x, gridDim.x, smem, ids);
+  prefill_body<HD, CHECK, NARROW, KV8, PACK>(a, blockIdx.x, gridDim.x, smem, ids);
 }
 
 }  // namespace pkv
@@ -140,8 +144,12 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
     return PKV_ERR_INVALID_ARG;
   for (const void* p : {static_cast<const void*>(out), query, key_pool, value_pool})
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PKV_ERR_INVALID_ARG;
-  const int q_tiles = (max_q_len + kPreTile - 1) / kPreTile;
-  const int64_t row_items = static_cast<int64_t>(num_seqs) * num_q_heads * q_tiles;
+  const int group = num_q_heads / num_kv_heads;
+  const bool pack = pkv_pre::pack_rows(max_q_len, num_q_heads, num_kv_heads);
+  const int64_t q_tiles64 = pkv_pre::row_tiles(max_q_len, pack ? group : 1);
+  if (q_tiles64 > (1 << 22)) return PKV_ERR_UNSUPPORTED;
+  const int q_tiles = static_cast<int>(q_tiles64);
+  const int64_t row_items = static_cast<int64_t>(num_seqs) * (pack ? num_kv_heads : num_q_heads) * q_tiles;
   const int ksplit = pkv_pre::ksplit_for(row_items, max_blocks_per_seq, head_dim, pkv_host::cu_count());
   const int64_t items = row_items * ksplit;
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
@@ -149,22 +157,24 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
   if (ksplit > 1 && (!workspace || workspace_bytes < lay.total)) return PKV_ERR_WORKSPACE_TOO_SMALL;
   if (ksplit > 1 && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PKV_ERR_INVALID_ARG;
   char* ws = static_cast<char*>(workspace);
-  const int group = num_q_heads / num_kv_heads;
   const float scale_log2 = kv8 ? scale * kLog2e * k_scale : scale * kLog2e;
   const float vs = kv8 ? v_scale : 1.f;
   const int ob = out_dtype == PKV_DTYPE_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool narrow = pkv_host::narrow_addressing(num_blocks, num_kv_heads, head_dim, kv8 ? 1 : 2);
-  const PreArgs pa{static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
+  PreArgs pa{static_cast<const uint16_t*>(query), cu_q_lens, chunk_offsets, key_pool, value_pool, block_tables,
                    max_blocks_per_seq, q_tiles, num_q_heads, num_kv_heads, group, num_blocks, causal != 0,
                    scale_log2, vs, out, ob, err_flag, ksplit,
                    ksplit > 1 ? reinterpret_cast<float*>(ws + lay.o) : nullptr,
                    ksplit > 1 ? reinterpret_cast<float*>(ws + lay.ml) : nullptr};
-#define PKV_PRE(HD, CHECK, NARROW, KV8)                                                                  \
-  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK, NARROW, KV8>), dim3(static_cast<unsigned>(items)), \
+  pa.pack = pack;
+#define PKV_PRE(HD, CHECK, NARROW, KV8, PACK)                                                                  \
+  hipLaunchKernelGGL((prefill_bf16_kernel<HD, CHECK, NARROW, KV8, PACK>), dim3(static_cast<unsigned>(items)), \
                      dim3(kPreThreads), 0, st, pa)
+#define PKV_PRE_P(HD, CHECK, NARROW, KV8) \
+  if (pack) PKV_PRE(HD, CHECK, NARROW, KV8, true); else PKV_PRE(HD, CHECK, NARROW, KV8, false);
 #define PKV_PRE_K(HD, CHECK, NARROW) \
-  if (kv8) PKV_PRE(HD, CHECK, NARROW, true); else PKV_PRE(HD, CHECK, NARROW, false);
+  if (kv8) { PKV_PRE_P(HD, CHECK, NARROW, true) } else { PKV_PRE_P(HD, CHECK, NARROW, false) }
 #define PKV_PRE_N(HD, CHECK) \
   if (narrow) { PKV_PRE_K(HD, CHECK, true) } else { PKV_PRE_K(HD, CHECK, false) }
 #define PKV_PRE_HD(CHECK)                         \
@@ -177,6 +187,7 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* query, const
 #undef PKV_PRE_HD
 #undef PKV_PRE_N
 #undef PKV_PRE_K
+#undef PKV_PRE_P
 #undef PKV_PRE
   if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
   if (ksplit > 1) {
@@ -207,9 +218,19 @@ extern "C" size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_q_le
   if (num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
       (head_dim != 64 && head_dim != 128 && head_dim != 256))
     return 0;
-  const int64_t row_items = static_cast<int64_t>(num_seqs) * num_q_heads * ((max_q_len + kPreTile - 1) / kPreTile);
-  const int ksplit = pkv_pre::ksplit_for(row_items, max_blocks_per_seq, head_dim, pkv_host::cu_count());
-  return pkv_pre::layout(row_items, ksplit, head_dim).total;
+  // The row layout depends on the KV head count, which this query does not take: the bound over
+  // every count that divides num_q_heads.
+  size_t most = 0;
+  for (int32_t hkv = 1; hkv <= num_q_heads; ++hkv) {
+    if (num_q_heads % hkv != 0) continue;
+    const bool pack = pkv_pre::pack_rows(max_q_len, num_q_heads, hkv);
+    const int64_t row_items = static_cast<int64_t>(num_seqs) * (pack ? hkv : num_q_heads) *
+                              pkv_pre::row_tiles(max_q_len, pack ? num_q_heads / hkv : 1);
+    const int ksplit = pkv_pre::ksplit_for(row_items, max_blocks_per_seq, head_dim, pkv_host::cu_count());
+    const size_t b = pkv_pre::layout(row_items, ksplit, head_dim).total;
+    most = b > most ? b : most;
+  }
+  return most;
 }
 
 extern "C" pkv_status pkv_paged_attn_prefill_chunk_fp8(void* out, pkv_dtype out_dtype, const void* query,

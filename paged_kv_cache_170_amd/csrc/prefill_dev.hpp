@@ -63,14 +63,20 @@ struct PreArgs {
   // prefix_slots slots per (sequence, query head)).
   const int32_t* prefix_members;
   int num_members, prefix_blocks, prefix_slots, prefix_slot0, prefix_num_seqs;
+  // Row layout of the items (prefill_body's PACK), read by the merge.
+  int pack;
 };
 
-// One work item (one key split of 256 query rows of one query head) on a 512-thread workgroup.
+// One work item (one key split of 256 rows) on a 512-thread workgroup.  Rows: with PACK false, the
+// chunk positions of one query head (row R = position R); with PACK true, the (position, query head)
+// pairs of one KV head's group (row R = position R / G, query head g*G + R % G), so that one item's
+// K/V tiles serve the whole group however short the chunk; shared-prefix rows are always (member,
+// query head) pairs.
 // id / items: the item's index among `items` consecutive workgroups (the remap below assumes
 // workgroups are dealt round-robin over the 8 XCDs starting at an XCD boundary, and keeps the
 // splits of a row tile next to each other, on one XCD).  smem holds PreCfg<HD>::LDS bytes and ids
 // kIdWindow ints (the block ids of logical blocks [win0, win0 + kIdWindow)).
-template <int HD, bool CHECK, bool NARROW, bool KV8>
+template <int HD, bool CHECK, bool NARROW, bool KV8, bool PACK>
 __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int items, char* smem, int* ids) {
   constexpr int E = KV8 ? 1 : 2;
   using C = PreCfg<HD, E>;
@@ -95,8 +101,8 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   const bool prefix = A_.prefix_members != nullptr;
   const int t = w % q_tiles;
   int r = w / q_tiles;
-  const int hi = prefix ? 0 : r % group;
-  r = prefix ? r : r / group;
+  const int hi = (PACK || prefix) ? 0 : r % group;
+  r = (PACK || prefix) ? r : r / group;
   const int g = r % num_kv_heads;
   const int s = prefix ? A_.prefix_members[0] : r / num_kv_heads;
   if (prefix && (s < 0 || s >= A_.prefix_num_seqs)) {
@@ -106,17 +112,22 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
   const int h = g * group + hi;
 
   const int qlo = prefix ? 0 : cu_q_lens[s];
-  const int L = prefix ? A_.num_members * group : cu_q_lens[s + 1] - qlo;
+  // PACK: the chunk's positions; rows L = positions x G.  Otherwise rows are positions (shared-prefix
+  // rows: members x G).
+  const int npos = prefix ? A_.num_members : cu_q_lens[s + 1] - qlo;
+  const int L = PACK ? npos * group : (prefix ? A_.num_members * group : cu_q_lens[s + 1] - qlo);
   const int off = prefix ? 0 : chunk_offsets[s];
   const int row0 = t * kPreTile;
   if (row0 >= L) return;
-  if (off < 0 || static_cast<int64_t>(off) + L > static_cast<int64_t>(max_blocks) * kBlockSize) {
+  if (off < 0 || static_cast<int64_t>(off) + (PACK ? npos : L) > static_cast<int64_t>(max_blocks) * kBlockSize) {
     if (!prefix) {
       if (CHECK && threadIdx.x == 0 && t == 0 && hi == 0) atomicOr(err_flag, PKV_FLAG_BAD_LENGTH);
       return;
     }
   }
-  const int kv_end = prefix ? A_.prefix_blocks * kBlockSize : causal ? off + min(row0 + kPreTile, L) : off + L;
+  const int kv_end = prefix   ? A_.prefix_blocks * kBlockSize
+                     : causal ? off + (PACK ? (min(row0 + kPreTile, L) - 1) / group + 1 : min(row0 + kPreTile, L))
+                              : off + (PACK ? npos : L);
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int qc = lane & 31, hh = lane >> 5;
@@ -130,14 +141,18 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
     p_seq = -1;
   }
   const bool row_ok = myrow < L && p_seq >= 0;
-  const int qpos = off + myrow;
-  const int p_head = prefix ? g * group + myrow % group : h;
+  // This row's chunk position and query head (p_head); with PACK, the first and last positions of
+  // the wave's rows for the causal skip and the edge-tile test.
+  const int mypos = PACK ? myrow / group : myrow;
+  const int qpos = off + mypos;
+  const int p_head = (PACK || prefix) ? g * group + myrow % group : h;
+  const int wave_pos0 = PACK ? wrow0 / group : 0, wave_pos1 = PACK ? (min(wrow0 + kPreRows, L) - 1) / group : 0;
 
   // Q^T as the B operand: lane (qc, hh) holds query row qc, head_dim 16ks + 8hh .. +7.
   bf16x8 qf[C::KS];
   {
     const int64_t qr = prefix ? static_cast<int64_t>(row_ok ? p_seq : 0) * num_q_heads + p_head
-                              : static_cast<int64_t>(qlo + (row_ok ? myrow : 0)) * num_q_heads + h;
+                              : static_cast<int64_t>(qlo + (row_ok ? mypos : 0)) * num_q_heads + (PACK ? p_head : h);
     const uint16_t* qrow = query + qr * HD + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = row_ok ? as_bf16x8(ld16(qrow + 16 * ks)) : bf16x8{};
@@ -247,7 +262,7 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
     for (int tt = 0; tt < 2; ++tt) {
     const int kt = 2 * pr + tt;
     const int key0 = kt * C::KT;
-    const bool active = kt < ntiles && wrow0 < L && (!causal || key0 <= off + wrow0 + kPreRows - 1);
+    const bool active = kt < ntiles && wrow0 < L && (!causal || key0 <= off + (PACK ? wave_pos1 : wrow0 + kPreRows - 1));
     if (active) {
       const char* tile = smem + (2 * cur + tt) * C::TILE;
       floatx16 sacc[C::MS];
@@ -276,7 +291,7 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // Element e = 4i + j of sacc[ms] is key key0 + 32ms + 8i + 4hh + j for query row qc.  Only
       // tiles that cross the causal diagonal or the end of the keys need the mask.
-      const bool edge = key0 + C::KT > kv_end || (causal && key0 + C::KT - 1 > off + wrow0);
+      const bool edge = key0 + C::KT > kv_end || (causal && key0 + C::KT - 1 > off + (PACK ? wave_pos0 : wrow0));
       if (edge) {
 #pragma unroll
         for (int ms = 0; ms < C::MS; ++ms)
@@ -382,7 +397,7 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
       return;
     }
   }
-  const int64_t obase = (static_cast<int64_t>(qlo + myrow) * num_q_heads + h) * HD;
+  const int64_t obase = (static_cast<int64_t>(qlo + mypos) * num_q_heads + (PACK ? p_head : h)) * HD;
   auto write_rows = [&](float ia) {
 #pragma unroll
     for (int md = 0; md < C::MD; ++md)
@@ -428,6 +443,20 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
 
 // Host helpers shared by the prefill and mixed-step entry points.
 namespace pkv_pre {
+
+// Row tiles of one (sequence, head) with PACK false, or of one (sequence, KV head) with PACK true:
+// max_q_len positions times the query heads sharing the rows, in tiles of kPreTile rows.
+inline int64_t row_tiles(int32_t max_q_len, int32_t heads_per_row_set) {
+  return (static_cast<int64_t>(max_q_len) * heads_per_row_set + pkv::kPreTile - 1) / pkv::kPreTile;
+}
+
+// Whether to pack the rows by KV head: only when that gives fewer row tiles (short chunks, or
+// chunks well short of a multiple of kPreTile); otherwise the per-head layout is kept.
+inline bool pack_rows(int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
+  const int32_t group = num_q_heads / num_kv_heads;
+  return group > 1 &&
+         num_kv_heads * row_tiles(max_q_len, group) < static_cast<int64_t>(num_q_heads) * row_tiles(max_q_len, 1);
+}
 
 // Key splits of a row tile: enough workgroups to give every CU one (each takes a whole CU's LDS),
 // at most kPreMaxSplit, and no more than the tile pairs the longest possible context has.
