@@ -15,8 +15,9 @@ p90.  The same steps run back to back without the flush ("hot") are reported bes
 
 Printed: one JSON line.  `value` is the decode KV-read bandwidth in GB/s over unique pool bytes
 (the shared prefix counted once) at the median flushed decode call (plan, attention and reduce);
-the prefill chunk's TFLOP/s, both fractions of peak, the hot figures and the two small configs
-(tiny fp32 decode, 1000-token chunked prefill) are in `secondary`; `roofline` describes the
+the prefill chunk's TFLOP/s, both fractions of peak, the hot figures, the two small configs
+(tiny fp32 decode, 1000-token chunked prefill) and a batch of short prefill chunks (32 prompts x
+32 tokens at offset 2,048) are in `secondary`; `roofline` describes the
 kernel that takes the most time per step, at its average flushed duration.  `cpu_baseline` times
 the fp64 oracle on this host on the same inputs (decode of every sequence, prefill of a sample of
 rows), with the small configs' oracle times (all host threads and one thread) beside it.
@@ -63,7 +64,7 @@ def parse():
     ap.add_argument("--no-flush", action="store_true",
                     help="time the steps without the cache flush (for profilers that count every launch)")
     ap.add_argument("--no-small-configs", action="store_true",
-                    help="skip the tiny-decode and chunked-prefill configs reported in secondary")
+                    help="skip the tiny-decode, chunked-prefill and short-chunk batch reported in secondary")
     ap.add_argument("--cpu-sample-rows", type=int, default=64, help="prefill rows timed in the oracle baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain fp32 copy kernel over this many MiB (a known-size reference "
@@ -522,6 +523,7 @@ def main():
     if not args.no_small_configs and not fp8 and args.workload == "mixed_step":
         small = small_configs(pkv, torch, dev, flush_bytes=0 if args.no_flush else 1 << 30)
         secondary["small_configs"] = small["gpu"]
+        secondary["short_chunk_batch"] = short_chunk_batch(pkv, torch, dev, flush_bytes=0 if args.no_flush else 1 << 30)
 
     cpu = None
     if fp8:
@@ -641,6 +643,48 @@ def small_configs(pkv, torch, dev, flush_bytes, runs=20):
                               "prefill_frac_mfma_peak": fl / (att * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS}
     del flush_buf
     return {"gpu": gpu, "c1": c1, "c2": c2, "c1_bytes": c1_bytes, "c2_flop": fl}
+
+
+def short_chunk_batch(pkv, torch, dev, flush_bytes, runs=20, num_seqs=32, chunk=32, offset=2048):
+    """A batch of short prefill chunks, as a continuous-batching step with chunked prefill carries
+    them: 32 prompts, each a 32-token chunk at offset 2,048 (so 2,080 cached positions each), the
+    mixed step's 64/8 x 128 bf16 heads.  Median over `runs` calls, each after the flush, of the
+    chunk call (HIP events); TFLOP/s over the causal algorithmic flops, GB/s over the K/V bytes the
+    chunks attend to.  Synthetic N(0,1) pools with a shuffled block table."""
+    hq, hkv, hd = 64, 8, 128
+    ctx = offset + chunk
+    nb = -(-ctx // 16)
+    nblk = nb * num_seqs + 8
+    g = torch.Generator(device="cpu").manual_seed(7)
+    kp = torch.randn((nblk, hkv, 16, hd), generator=g).to(torch.bfloat16).to(dev)
+    vp = torch.randn((nblk, hkv, 16, hd), generator=g).to(torch.bfloat16).to(dev)
+    bt = torch.randperm(nblk, generator=g)[: nb * num_seqs].to(torch.int32).reshape(num_seqs, nb).contiguous().to(dev)
+    q = torch.randn((num_seqs * chunk, hq, hd), generator=g).to(torch.bfloat16).to(dev)
+    cu = torch.arange(0, num_seqs * chunk + 1, chunk, dtype=torch.int32).to(dev)
+    offs = torch.full((num_seqs,), offset, dtype=torch.int32).to(dev)
+    ws = pkv.prefill_workspace(q, num_seqs, chunk, nb)
+    scale = 1.0 / math.sqrt(hd)
+    out = pkv.paged_attn_prefill_chunk(q, cu, offs, kp, vp, bt, chunk, scale, causal=True, workspace=ws)
+    flush_buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device=dev) if flush_bytes else None
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for r in range(runs + 2):
+        if flush_buf is not None:
+            torch.amax(flush_buf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pkv.paged_attn_prefill_chunk(q, cu, offs, kp, vp, bt, chunk, scale, causal=True, out=out, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r >= 2:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    flop = 4 * hd * hq * num_seqs * (chunk * offset + chunk * (chunk + 1) // 2)
+    kv_bytes = num_seqs * ctx * 2 * hkv * hd * 2
+    del flush_buf
+    return {"config": f"{num_seqs} chunks of {chunk} tokens at offset {offset}, {hq}/{hkv} heads x {hd}, bf16",
+            "ms": ms, "tflops": flop / (ms * 1e-3) / 1e12, "kv_gbs": kv_bytes / (ms * 1e-3) / 1e9,
+            "kv_frac_hbm_peak": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def small_configs_oracle(small):
