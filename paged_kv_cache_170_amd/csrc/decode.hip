@@ -110,13 +110,20 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(const int32_t
 }
 
 // Persistent decode kernel: one worker per workgroup (see decode_worker).
-template <int HD, bool CHECK, bool NARROW, bool KV8>
+// PLANNED false: a small batch without a plan pass (see decode_worker).
+template <int HD, bool CHECK, bool NARROW, bool KV8, bool PLANNED>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(HD > 128 ? 1 : 2))) void decode_bf16_kernel(DecArgs a, const int2* __restrict__ pieces,
                                                                   int32_t* __restrict__ plan, int queues) {
   __shared__ __attribute__((aligned(16))) char smem[DecCfg<HD>::LDS];
   __shared__ int fetched[2];
   WgSync sync;
-  decode_worker<HD, CHECK, NARROW, KV8>(a, pieces, plan, queues, blockIdx.x, gridDim.x, smem, fetched, sync);
+  if constexpr (PLANNED) {
+    decode_worker<HD, CHECK, NARROW, KV8>(a, pieces, plan, queues, blockIdx.x, gridDim.x, smem, fetched, sync);
+  } else {
+    __shared__ int scan[2 * kWave];
+    decode_worker<HD, CHECK, NARROW, KV8, false>(a, pieces, plan, queues, blockIdx.x, gridDim.x, smem, fetched, sync,
+                                                 scan);
+  }
 }
 
 // fp32 pools: VALU kernel.  A wave step covers 32 positions; lanes 0-31 and 32-63 each take one
@@ -462,14 +469,21 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* query, const 
     const unsigned nwg = static_cast<unsigned>(max_items < resident ? max_items : resident);
     const int queues = nwg % kMaxQueues == 0 ? kMaxQueues : (nwg % 8 == 0 ? 8 : 1);
     const bool narrow = pkv_host::narrow_addressing(num_blocks, num_kv_heads, head_dim, kv8 ? 1 : 2);
-    launch_plan(err_flag != nullptr, context_lens, num_seqs, max_blocks_per_seq, S, pieces, plan,
-                static_cast<int>(nwg), queues, err_flag, st);
-    if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
-#define PKV_DEC_BF16(HD, CHECK, NARROW, KV8)                                                                    \
-  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW, KV8>), dim3(nwg), dim3(kDecThreads), 0, st, a, pieces, \
-                     plan, queues)
+    // A small batch whose every possible item has a workgroup of its own needs no plan: each
+    // workgroup finds its item from the context lengths, and the plan launch is saved.
+    const bool planned = !(num_seqs <= kWave && max_items <= resident);
+    if (planned) {
+      launch_plan(err_flag != nullptr, context_lens, num_seqs, max_blocks_per_seq, S, pieces, plan,
+                  static_cast<int>(nwg), queues, err_flag, st);
+      if (pkv_host::launch_status() != PKV_OK) return PKV_ERR_HIP;
+    }
+#define PKV_DEC_BF16P(HD, CHECK, NARROW, KV8, PLANNED)                                                            \
+  hipLaunchKernelGGL((decode_bf16_kernel<HD, CHECK, NARROW, KV8, PLANNED>), dim3(nwg), dim3(kDecThreads), 0, st, a, \
+                     pieces, plan, queues)
+#define PKV_DEC_BF16(HD, CHECK, NARROW, KV8) \
+  if (planned) PKV_DEC_BF16P(HD, CHECK, NARROW, KV8, true); else PKV_DEC_BF16P(HD, CHECK, NARROW, KV8, false);
 #define PKV_DEC_BF16_K(HD, CHECK, NARROW) \
-  if (kv8) PKV_DEC_BF16(HD, CHECK, NARROW, true); else PKV_DEC_BF16(HD, CHECK, NARROW, false);
+  if (kv8) { PKV_DEC_BF16(HD, CHECK, NARROW, true) } else { PKV_DEC_BF16(HD, CHECK, NARROW, false) }
 #define PKV_DEC_BF16_N(HD, CHECK) \
   if (narrow) { PKV_DEC_BF16_K(HD, CHECK, true) } else { PKV_DEC_BF16_K(HD, CHECK, false) }
 #define PKV_DEC_BF16_C(HD) \
@@ -483,6 +497,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* query, const 
 #undef PKV_DEC_BF16_N
 #undef PKV_DEC_BF16_K
 #undef PKV_DEC_BF16
+#undef PKV_DEC_BF16P
   } else {
     if (err_flag) { PKV_DEC_HD(decode_f32_kernel, float, true) } else { PKV_DEC_HD(decode_f32_kernel, float, false) }
   }

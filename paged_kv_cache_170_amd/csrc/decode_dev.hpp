@@ -406,20 +406,55 @@ constexpr int kMaxClasses = 2048 / 32 + 1;
 // worker / nworkers: this worker's index in the persistent grid and the grid's size (the workgroup
 // index and count, or two workers per workgroup in the fused mixed-step kernel); smem holds
 // DecCfg<HD>::LDS bytes and fetched two ints, both private to the worker.
-template <int HD, bool CHECK, bool NARROW, bool KV8, class Sync>
+// PLANNED false (no plan pass; at most 64 sequences, no shared-prefix members, and a worker for every
+// possible item, so that each worker runs at most one item): the worker finds its item from the
+// context lengths itself — sequence-major pieces, item i = piece i / Hkv, KV head i % Hkv — through a
+// prefix sum of the pieces per sequence kept in `scan` (2 x 64 ints of LDS).
+template <int HD, bool CHECK, bool NARROW, bool KV8, bool PLANNED = true, class Sync>
 __device__ __forceinline__ void decode_worker(const DecArgs& a, const int2* __restrict__ pieces,
                                               int32_t* __restrict__ plan, int queues, int worker, int nworkers,
-                                              char* smem, int* fetched, Sync& sync) {
+                                              char* smem, int* fetched, Sync& sync, int* scan = nullptr) {
   const int tid = threadIdx.x & (kDecThreads - 1);
   const int queue = worker % queues;
-  const int total = plan[kPlanTotal] * a.num_kv_heads;
+  int total;
+  if constexpr (PLANNED) {
+    total = plan[kPlanTotal] * a.num_kv_heads;
+  } else {
+    // Pieces per sequence: its splits, or one for an empty sequence (which writes zeros).
+    if (tid < kWave) {
+      const int ctx =
+          tid < a.num_seqs ? clamp_ctx<CHECK>(a.context_lens[tid], a.max_blocks, a.err_flag, worker == 0) : 0;
+      const int n = tid < a.num_seqs ? (ctx > 0 ? (ctx + a.split_tokens - 1) / a.split_tokens : 1) : 0;
+      int incl = n;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (tid >= off) incl += v;
+      }
+      scan[tid] = incl;
+      scan[kWave + tid] = ctx;
+    }
+    sync();
+    total = scan[kWave - 1] * a.num_kv_heads;
+  }
   auto find = [&](int item, DecItem<HD>& it) {
     const int piece = item / a.num_kv_heads;
-    const int2 code = pieces[piece];
-    it.s = static_cast<int>(static_cast<uint32_t>(code.x) >> 16);
-    it.split = code.x & 0xffff;
+    if constexpr (PLANNED) {
+      const int2 code = pieces[piece];
+      it.s = static_cast<int>(static_cast<uint32_t>(code.x) >> 16);
+      it.split = code.x & 0xffff;
+      it.ctx = code.y;
+    } else {
+      // First sequence whose inclusive piece count passes `piece` (binary search over 64 entries).
+      int lo = 0;
+#pragma unroll
+      for (int step = kWave / 2; step > 0; step >>= 1)
+        if (scan[lo + step - 1] <= piece) lo += step;
+      it.s = lo;
+      it.split = piece - (lo > 0 ? scan[lo - 1] : 0);
+      it.ctx = scan[kWave + lo];
+    }
     it.g = item - piece * a.num_kv_heads;
-    it.ctx = code.y;
     it.nsplit = (it.ctx + a.split_tokens - 1) / a.split_tokens;
     it.tbl0 = (a.member != nullptr && a.member[it.s]) ? a.prefix_blocks : 0;
   };
@@ -438,7 +473,7 @@ __device__ __forceinline__ void decode_worker(const DecArgs& a, const int2* __re
     int ticket = 0;
     auto fetch_next = [&]() {
       if (have_next) {
-        if (tid == 0) ticket = atomicAdd(&plan[queue * kCounterStride], 1);
+        if (PLANNED && tid == 0) ticket = atomicAdd(&plan[queue * kCounterStride], 1);
         find(nxt_i, nxt);
         decode_item_prologue<HD, CHECK>(a, nxt);  // in flight while this item runs
       }
