@@ -16,8 +16,8 @@ p90.  The same steps run back to back without the flush ("hot") are reported bes
 Printed: one JSON line.  `value` is the decode KV-read bandwidth in GB/s over unique pool bytes
 (the shared prefix counted once) at the median flushed decode call (plan, attention and reduce);
 the prefill chunk's TFLOP/s, both fractions of peak, the hot figures, the two small configs
-(tiny fp32 decode, 1000-token chunked prefill) and a batch of short prefill chunks (32 prompts x
-32 tokens at offset 2,048) are in `secondary`; `roofline` describes the
+(tiny fp32 decode, 1000-token chunked prefill), a batch of short prefill chunks (32 prompts x
+32 tokens at offset 2,048) and the decode of one 32,768-position sequence are in `secondary`; `roofline` describes the
 kernel that takes the most time per step, at its average flushed duration.  `cpu_baseline` times
 the fp64 oracle on this host on the same inputs (decode of every sequence, prefill of a sample of
 rows), with the small configs' oracle times (all host threads and one thread) beside it.
@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--no-flush", action="store_true",
                     help="time the steps without the cache flush (for profilers that count every launch)")
     ap.add_argument("--no-small-configs", action="store_true",
-                    help="skip the tiny-decode, chunked-prefill and short-chunk batch reported in secondary")
+                    help="skip the tiny-decode, chunked-prefill, short-chunk and single-sequence runs in secondary")
     ap.add_argument("--cpu-sample-rows", type=int, default=64, help="prefill rows timed in the oracle baseline")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run a plain fp32 copy kernel over this many MiB (a known-size reference "
@@ -524,6 +524,8 @@ def main():
         small = small_configs(pkv, torch, dev, flush_bytes=0 if args.no_flush else 1 << 30)
         secondary["small_configs"] = small["gpu"]
         secondary["short_chunk_batch"] = short_chunk_batch(pkv, torch, dev, flush_bytes=0 if args.no_flush else 1 << 30)
+        secondary["single_sequence_decode"] = single_sequence_decode(pkv, torch, dev,
+                                                                     flush_bytes=0 if args.no_flush else 1 << 30)
 
     cpu = None
     if fp8:
@@ -685,6 +687,41 @@ def short_chunk_batch(pkv, torch, dev, flush_bytes, runs=20, num_seqs=32, chunk=
     return {"config": f"{num_seqs} chunks of {chunk} tokens at offset {offset}, {hq}/{hkv} heads x {hd}, bf16",
             "ms": ms, "tflops": flop / (ms * 1e-3) / 1e12, "kv_gbs": kv_bytes / (ms * 1e-3) / 1e9,
             "kv_frac_hbm_peak": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def single_sequence_decode(pkv, torch, dev, flush_bytes, runs=20, ctx=32768):
+    """Decode latency of one long request: one sequence at 32,768 cached positions, the mixed
+    step's 64/8 x 128 bf16 heads (134 MB of K/V).  Median over `runs` calls, each after the flush
+    (HIP events); GB/s over the K/V bytes.  Synthetic N(0,1) pools with a shuffled block table."""
+    hq, hkv, hd = 64, 8, 128
+    nb = -(-ctx // 16)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    kp = torch.randn((nb + 8, hkv, 16, hd), generator=g).to(torch.bfloat16).to(dev)
+    vp = torch.randn((nb + 8, hkv, 16, hd), generator=g).to(torch.bfloat16).to(dev)
+    bt = torch.randperm(nb + 8, generator=g)[:nb].to(torch.int32).reshape(1, nb).contiguous().to(dev)
+    q = torch.randn((1, hq, hd), generator=g).to(torch.bfloat16).to(dev)
+    cl = torch.full((1,), ctx, dtype=torch.int32).to(dev)
+    ws = pkv.decode_workspace(q, hkv, nb)
+    scale = 1.0 / math.sqrt(hd)
+    out = pkv.paged_attn_decode(q, kp, vp, bt, cl, scale, workspace=ws)
+    flush_buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device=dev) if flush_bytes else None
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for r in range(runs + 2):
+        if flush_buf is not None:
+            torch.amax(flush_buf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pkv.paged_attn_decode(q, kp, vp, bt, cl, scale, out=out, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r >= 2:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    kv_bytes = ctx * 2 * hkv * hd * 2
+    del flush_buf
+    return {"config": f"1 sequence at {ctx} positions, {hq}/{hkv} heads x {hd}, bf16", "ms": ms,
+            "kv_gbs": kv_bytes / (ms * 1e-3) / 1e9, "kv_frac_hbm_peak": kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def small_configs_oracle(small):
