@@ -416,13 +416,12 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
         }
       }
   };
-  if (HD > 128 || ksplit == 1) {
+  if (ksplit == 1) {
     if (!row_ok) return;
     const float inv = l_run > 0.f ? v_scale / l_run : 0.f;
     write_rows(inv);
     return;
   }
-  if constexpr (HD <= 128) {
   // Several splits: write this split's (o, m, l) partial; prefill_merge_kernel combines them
   // after the launch (the kernel boundary orders the writes before the reads on every XCD).
   const int prow = wave * kPreRows + qc;  // row inside the tile
@@ -436,7 +435,6 @@ __device__ __forceinline__ void prefill_body(const PreArgs& A_, int id, int item
       *reinterpret_cast<float4*>(my_o + d) = float4{acc[md][4 * i], acc[md][4 * i + 1], acc[md][4 * i + 2], acc[md][4 * i + 3]};
     }
   if (hh == 0) *reinterpret_cast<float2*>(A_.ws_ml + part * 2) = float2{m_ref, l_run};
-  }
 }
 
 }  // namespace pkv
@@ -461,8 +459,7 @@ inline bool pack_rows(int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_hea
 // Key splits of a row tile: enough workgroups to give every CU one (each takes a whole CU's LDS),
 // at most kPreMaxSplit, and no more than the tile pairs the longest possible context has.
 inline int ksplit_for(int64_t row_items, int32_t max_blocks, int32_t head_dim, int cus) {
-  // head_dim 256 keeps one split: its registers leave no room for the merge.
-  if (row_items <= 0 || head_dim > 128) return 1;
+  if (row_items <= 0) return 1;
   int64_t k = (cus + row_items - 1) / row_items;
   const int kt = head_dim == 256 ? 32 : 64;
   const int64_t pairs = (static_cast<int64_t>(max_blocks) * pkv::kBlockSize + 2 * kt - 1) / (2 * kt);

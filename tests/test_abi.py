@@ -123,7 +123,7 @@ def test_host_validation_rejects_bad_arguments():
     # refuses a missing workspace when one is needed.
     pwb = lib.pkv_prefill_workspace_bytes
     assert pwb(1, 512, 64, 128, 2048) > 0 and pwb(64, 4096, 64, 128, 2048) == 0 and pwb(1, 512, 64, 96, 64) == 0
-    assert pwb(1, 512, 4, 256, 2048) == 0  # head_dim 256 never splits
+    assert pwb(1, 512, 4, 256, 2048) > 0 and pwb(64, 4096, 64, 256, 2048) == 0  # head_dim 256 splits too
     fake = ctypes.c_void_p(16)
     assert pre(fake, 0, fake, fake, fake, fake, fake, fake, 2048, 1, 512, 64, 8, 128, 10, 1, 0.1, 1, null, 0, null,
                null) == 3
