@@ -338,8 +338,9 @@ def main():
     torch.cuda.synchronize()
     stream_gbs = 5 * kp.numel() * kp.element_size() / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
-    # Rate a kernel of pure bf16 MFMA work reaches on this device (every SIMD issuing independent
-    # 32x32x16 MFMAs and nothing else), run for about as long as the prefill chunk takes.
+    # Rate a kernel of pure bf16 MFMA work reaches on this device (every SIMD issuing 32x32x16
+    # MFMAs on operands that change from one MFMA to the next, and nothing else), run for about as
+    # long as the prefill chunk takes.
     mfma_loop = None
     if pre is not None:
         msink = torch.zeros(1, dtype=torch.float32, device=dev)

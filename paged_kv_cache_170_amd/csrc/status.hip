@@ -78,21 +78,42 @@ extern "C" pkv_status pkv_stream_read_probe(const void* buf, size_t bytes, uint3
 // Matrix-core reference: independent MFMA chains on every SIMD, nothing else (see pagedkv.h).
 namespace {
 __global__ __launch_bounds__(512) void mfma_peak_kernel(int iters, float* __restrict__ sink) {
-  const int t = threadIdx.x;
-  pkv::bf16x8 x, y;
+  // Eight A and eight B fragments of pseudo-random bf16 values in [-2, 2) per lane (a per-thread
+  // xorshift), so that consecutive MFMAs see different operands: the switching activity of real
+  // data, which sets the power, and so the clock, the matrix cores hold.  (Constant operands run
+  // at a markedly higher rate than any real kernel can.)
+  uint32_t h = (blockIdx.x * 512u + threadIdx.x) * 2654435761u + 0x9e3779b9u;
+  auto rnd = [&]() {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    return static_cast<__bf16>(static_cast<float>(static_cast<int32_t>(h)) * 0x1p-30f);
+  };
+  pkv::bf16x8 A[8], B[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[i] = static_cast<__bf16>(0.01f * static_cast<float>(t + i));
-    y[i] = static_cast<__bf16>(0.02f * static_cast<float>(i - t));
-  }
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      A[f][i] = rnd();
+      B[f][i] = rnd();
+    }
   pkv::floatx16 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
-  for (int it = 0; it < iters; ++it)
+  // Four independent accumulator chains; 64 MFMAs (16 iterations' worth) cycle through the 64
+  // operand pairs.
+  int it = 0;
+  for (; it + 16 <= iters; it += 16)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc[j], 0, 0, 0);
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+        acc[(a + b) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[a], B[b], acc[(a + b) & 3], 0, 0, 0);
+  for (; it < iters; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[j], B[j], acc[j], 0, 0, 0);
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
