@@ -126,3 +126,31 @@ def test_prefill_chunk_of_many_row_tiles(pkv, dev, mode):
     L, off = int(c.cu_q_lens[1]), int(c.chunk_offsets[0])
     _say(f"case prefill, one chunk of {L} rows ({-(-L // 256)} row tiles) at offset {off}, 4/1 heads x 64")
     _prefill_case_check(pkv, dev, mode, c)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_prefill_block_id_window_slides(pkv, dev, mode):
+    # The prefill stages the block ids of 2,048 blocks (32,768 positions) in LDS and moves that
+    # window on when a key split reads past it.  A 1,024-row chunk over 64 query heads gives 256
+    # row tiles, so one key split covers the whole context, here 35,538 positions (2,222 blocks).
+    # The oracle checks 24 rows (at the start, middle and end of the chunk) of every head.
+    c = wl.random_case(122, kind="prefill", dtype="bf16", num_seqs=1, num_q_heads=64, num_kv_heads=8, head_dim=64,
+                       max_ctx=41000, min_ctx=1024, q_len_max=1024, poison=True)
+    L, off = int(c.cu_q_lens[1]), int(c.chunk_offsets[0])
+    assert L == 1024 and off + L > 32768 + 1024, "the case must read past the first id window"
+    _say(f"case prefill, one chunk of {L} rows at offset {off} ({-(-(off + L) // 16)} blocks), 64/8 heads x 64")
+    assert pkv.prefill_workspace_bytes(1, L, 64, 64, c.block_tables.shape[1]) == 0  # one key split
+    d = Dev(c, dev)
+    err = new_err(dev, mode)
+    slots = write_new_tokens(pkv, d, err)
+    rk, rv = oracle_pools_after_write(c, slots)
+    out = pkv.paged_attn_prefill_chunk(to_dev(c.query, dev, c.dtype), to_dev(c.cu_q_lens, dev),
+                                       to_dev(c.chunk_offsets, dev), d.kp, d.vp, d.bt, L, c.scale, causal=True,
+                                       err_flag=err).cpu().numpy()
+    assert flag(err) == 0
+    for i0 in (0, 508, 1016):
+        sub = slice(i0, i0 + 8)
+        ref = oracle.prefill_chunk(c.query[sub], np.array([0, 8], np.int32), np.array([off + i0], np.int32), rk, rv,
+                                   c.block_tables, c.scale, c.dtype)
+        mx, mean = assert_close(out[sub], ref, c.dtype, f"prefill rows {i0}..{i0 + 7}")
+        _say(f"  rows {i0}..{i0 + 7}: max-abs {mx:.2e} mean-abs {mean:.2e}")
