@@ -154,3 +154,51 @@ def test_prefill_block_id_window_slides(pkv, dev, mode):
                                    c.block_tables, c.scale, c.dtype)
         mx, mean = assert_close(out[sub], ref, c.dtype, f"prefill rows {i0}..{i0 + 7}")
         _say(f"  rows {i0}..{i0 + 7}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+def _ramp_keys(c, top=4.0):
+    """Scale every live key row by 1 + (top - 1) * position / longest context (bf16, nearest-even),
+    so that scores keep growing along each sequence."""
+    kf = (c.key_pool.astype(np.uint32) << 16).view(np.float32)
+    lens = c.context_lens if c.kind == "decode" else c.chunk_offsets + np.diff(c.cu_q_lens)
+    longest = int(lens.max())
+    for s in range(c.num_seqs):
+        for j in range(int(lens[s])):
+            b = int(c.block_tables[s, j // 16])
+            kf[b, :, j % 16, :] *= np.float32(1.0 + (top - 1.0) * j / longest)
+    c.key_pool[...] = wl.f32_to_bf16_bits(kf)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_softmax_reference_raised_mid_sequence(pkv, dev, mode, kind):
+    # Scale 1.0 (scores of N(0,1) rows at head_dim 128 spread over about +-40 in log2 units) and
+    # keys that grow 4x along the context: later tiles keep holding weights far above 2^20 times
+    # the reference the earlier tiles set (up to exponentials that overflow), so the kernels take
+    # their raise-and-recompute path again and again, not only on the first tile.
+    if kind == "decode":
+        c = wl.random_case(76, kind="decode", dtype="bf16", num_seqs=6, num_q_heads=16, num_kv_heads=2,
+                           head_dim=128, max_ctx=3000, min_ctx=1500, poison=True, new_tokens=False)
+    else:
+        c = wl.random_case(77, kind="prefill", dtype="bf16", num_seqs=2, num_q_heads=16, num_kv_heads=2,
+                           head_dim=128, max_ctx=3000, min_ctx=100, q_len_max=300, poison=True, new_tokens=False)
+    _ramp_keys(c)
+    scale = 1.0
+    _say(f"case {kind}, keys ramped 1x..4x along the context, scale {scale}")
+    d = Dev(c, dev)
+    err = new_err(dev, mode)
+    q = to_dev(c.query, dev, c.dtype)
+    if kind == "decode":
+        ref = oracle.decode(c.query, c.key_pool, c.value_pool, c.block_tables, c.context_lens, scale, c.dtype)
+        outs = [pkv.paged_attn_decode(q, d.kp, d.vp, d.bt, d.ctx, scale, split_tokens=s, err_flag=err)
+                for s in (0, 256)]
+    else:
+        ref = oracle.prefill_chunk(c.query, c.cu_q_lens, c.chunk_offsets, c.key_pool, c.value_pool, c.block_tables,
+                                   scale, c.dtype)
+        maxl = int(np.diff(c.cu_q_lens).max())
+        outs = [pkv.paged_attn_prefill_chunk(q, to_dev(c.cu_q_lens, dev), to_dev(c.chunk_offsets, dev), d.kp, d.vp,
+                                             d.bt, maxl, scale, causal=True, err_flag=err)]
+    for i, o in enumerate(outs):
+        mx, mean = assert_close(o.cpu().numpy(), ref, c.dtype, f"{kind} #{i}")
+        _say(f"  #{i}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert flag(err) == 0
