@@ -517,11 +517,11 @@ pkv_status pkv_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, 
  * each) in four independent chains on register operands and nothing else.  The operands are eight
  * A and eight B fragments of pseudo-random bf16 values per lane, cycled so that consecutive MFMAs
  * see different data (the switching activity, and so the power and clock, of a real kernel's
- * operands; constant operands would run faster than any real kernel can).  *sink (a device float) is written
- * only if the sums take a value they never take, so the work is kept but nothing is stored.  Its
- * duration gives the bf16 MFMA rate a kernel of pure matrix work reaches on the device (its clock
- * under that load included), against which the prefill's rate is compared.  The flop count of one
- * call is cu_count x 8 waves x iters x 4 x 32,768.  iters must be positive.
+ * operands; constant operands would run faster than any real kernel can).  *sink (a device float)
+ * is written only if the sums take a value they never take, so the work is kept but nothing is
+ * stored.  Its duration gives the bf16 MFMA rate a kernel of pure matrix work reaches on the
+ * device (its clock under that load included), against which the prefill's rate is compared.  The
+ * flop count of one call is cu_count x 8 waves x iters x 4 x 32,768.  iters must be positive.
  */
 pkv_status pkv_mfma_peak_probe(int32_t iters, float* sink, void* stream);
 int32_t pkv_device_cu_count(void);
